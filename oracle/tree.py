@@ -1,0 +1,143 @@
+"""Static candidate tree, CPU oracle (test infrastructure only).
+
+Follows P1 ("Medusa 심층 아키텍처"), section "트리 어텐션 ... 고정 트리 토폴로지와
+2차원 어텐션 마스크": head d contributes its top candidates at depth d, a fixed
+topology combines them into paths, and the tree mask lets token i see token j
+iff j is an ancestor of i or j = i (0, else -inf).  P1's sketch code
+(``build_tree_attention_mask``) builds the same mask a second way: set the
+diagonal, then for each (child, parent) pair mark the parent and copy the
+parent's visible set into the child's row.
+
+Node numbering: node 0 is the root (the base model's token t+1); a node at
+depth d >= 1 carries candidate number rank(n) of Medusa head d (head index
+d-1), which predicts token t+d+1 (P1 section "Medusa의 핵심 철학", head list;
+P4 section 2.2).  Position of node n = ctx + depth(n).
+
+Reading: P1's sketch lost its indentation; the propagation is read as being
+inside the pair loop, which is correct when pairs arrive in topological order
+(parent before child).  We require parent[n] < n.
+"""
+from __future__ import annotations
+
+from typing import List, Sequence, Set
+
+import numpy as np
+
+
+def validate(parent: Sequence[int], rank: Sequence[int], k_per_depth: Sequence[int]) -> np.ndarray:
+    """Check the topology; return depth[T].  Raises ValueError if invalid."""
+    parent = [int(p) for p in parent]
+    rank = [int(r) for r in rank]
+    T = len(parent)
+    if T < 1 or len(rank) != T:
+        raise ValueError("need T >= 1 nodes and one rank per node")
+    if parent[0] != -1:
+        raise ValueError("node 0 must be the root (parent -1)")
+    depth = [0] * T
+    seen = set()
+    for n in range(1, T):
+        p = parent[n]
+        if not (0 <= p < n):
+            raise ValueError(f"parent[{n}]={p} is not an earlier node")
+        depth[n] = depth[p] + 1
+        if depth[n] > len(k_per_depth):
+            raise ValueError(f"node {n} is deeper than the number of heads")
+        if not (0 <= rank[n] < k_per_depth[depth[n] - 1]):
+            raise ValueError(f"rank[{n}]={rank[n]} outside head {depth[n]}'s top-k")
+        if (p, rank[n]) in seen:
+            raise ValueError(f"two children of node {p} share rank {rank[n]}")
+        seen.add((p, rank[n]))
+    return np.asarray(depth, dtype=np.int64)
+
+
+def ancestors_bruteforce(parent: Sequence[int]) -> List[Set[int]]:
+    """anc(i) by walking parent pointers from i to the root (i excluded)."""
+    out = []
+    for i in range(len(parent)):
+        s, u = set(), int(parent[i])
+        while u >= 0:
+            s.add(u)
+            u = int(parent[u])
+        out.append(s)
+    return out
+
+
+def visible_bruteforce(parent: Sequence[int]) -> np.ndarray:
+    """Boolean [T, T]: vis[i, j] iff j is an ancestor of i or j == i."""
+    T = len(parent)
+    vis = np.zeros((T, T), dtype=bool)
+    for i, s in enumerate(ancestors_bruteforce(parent)):
+        vis[i, i] = True
+        for j in s:
+            vis[i, j] = True
+    return vis
+
+
+def mask_by_propagation(pairs, total_tokens: int) -> np.ndarray:
+    """The additive mask [T, T] (0 visible, -inf hidden) built the way P1's
+    sketch code describes: diagonal first, then per (child, parent) pair in
+    topological order, mark the parent and inherit the parent's row."""
+    mask = np.full((total_tokens, total_tokens), -np.inf)
+    for i in range(total_tokens):
+        mask[i, i] = 0.0
+    for child, par in pairs:
+        mask[child, par] = 0.0
+        for k in range(total_tokens):
+            if mask[par, k] == 0.0:
+                mask[child, k] = 0.0
+    return mask
+
+
+def pairs_of(parent: Sequence[int]):
+    return [(n, int(parent[n])) for n in range(1, len(parent))]
+
+
+def bitmask_rows(vis: np.ndarray) -> np.ndarray:
+    """Pack a boolean [T, T] visibility matrix into uint64 words [T, ceil(T/64)]:
+    bit (j % 64) of word j // 64 in row i is vis[i, j]."""
+    T = vis.shape[0]
+    W = (T + 63) // 64
+    out = np.zeros((T, W), dtype=np.uint64)
+    for i in range(T):
+        for j in range(T):
+            if vis[i, j]:
+                out[i, j // 64] |= np.uint64(1) << np.uint64(j % 64)
+    return out
+
+
+def children_in_rank_order(parent: Sequence[int], rank: Sequence[int]) -> List[List[int]]:
+    T = len(parent)
+    kids: List[List[int]] = [[] for _ in range(T)]
+    for n in range(1, T):
+        kids[int(parent[n])].append(n)
+    for u in range(T):
+        kids[u].sort(key=lambda n: int(rank[n]))
+    return kids
+
+
+def tree_tokens(topk_idx: np.ndarray, root: Sequence[int], parent, rank) -> np.ndarray:
+    """tree_tokens[b, 0] = root[b]; tree_tokens[b, n] = topk_idx[b, depth(n)-1, rank(n)]."""
+    depth = depth_of(parent)
+    B = topk_idx.shape[0]
+    T = len(parent)
+    out = np.zeros((B, T), dtype=np.int64)
+    for b in range(B):
+        out[b, 0] = int(root[b])
+        for n in range(1, T):
+            out[b, n] = int(topk_idx[b, depth[n] - 1, int(rank[n])])
+    return out
+
+
+def positions(ctx_len: Sequence[int], parent) -> np.ndarray:
+    """pos[b, n] = ctx_len[b] + depth(n): node n sits depth(n) tokens after the
+    last cached token, whatever branch it is on."""
+    depth = depth_of(parent)
+    return np.asarray([[int(c) + int(d) for d in depth] for c in ctx_len], dtype=np.int64)
+
+
+def depth_of(parent) -> np.ndarray:
+    T = len(parent)
+    d = np.zeros(T, dtype=np.int64)
+    for n in range(1, T):
+        d[n] = d[int(parent[n])] + 1
+    return d

@@ -1,0 +1,366 @@
+"""Pins for the acceptance oracle.
+
+Greedy: the pages' worked examples (P3 section 5 rollback case; P4 section
+1.3), brute force over every root-to-leaf path, and the invariant that greedy
+speculation reproduces target-only greedy decoding token for token.
+
+Rejection: the statistical facts the pages state (P1 rejection-sampling
+section; P3 sections 2 and 5): the output is distributed as p (TVD within
+0.01 at 150k samples; chi-squared), a single draft is accepted with
+probability sum(min(p, q)), the expected tokens per step of a chain with
+constant acceptance alpha is (1 - alpha^(K+1)) / (1 - alpha), and the special
+cases p = q (always accept) and disjoint supports (always reject).  Drafts in
+these tests are sampled from q, which is what the losslessness argument
+assumes.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from medusa_tree_verification_amd import synth
+from oracle import accept, tree
+
+
+def _chain_logits(target_argmax, V):
+    """Base logits for a chain root->d1->...: row u peaks at target_argmax[u]."""
+    base = np.zeros((len(target_argmax), V))
+    for u, t in enumerate(target_argmax):
+        base[u, t] = 5.0
+    return base
+
+
+def _run_chain_greedy(drafts, target_argmax, V=64):
+    parent, rank = synth.chain_tree(len(drafts))
+    toks = np.array([0] + list(drafts))
+    base = _chain_logits(target_argmax[:len(drafts) + 1], V)
+    return accept.accept_greedy(base, toks, parent, rank)
+
+
+def test_page_rollback_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "p3_rollback_example.json")))
+    r = _run_chain_greedy(g["drafts"], g["target_argmax_after_prefix"])
+    assert r.tokens == g["expected_emitted"]
+    assert r.accept_len == g["expected_accept_len"]
+
+
+def test_page_verify_examples(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "p4_verify_examples.json")))
+    for case in g["cases"]:
+        r = _run_chain_greedy(case["drafts"], case["target_argmax_after_prefix"])
+        assert r.tokens == case["expected_emitted"], case["what"]
+        assert r.accept_len == case["expected_accept_len"]
+        assert r.nodes == list(range(r.accept_len + 1))
+
+
+def _paths(parent):
+    kids = tree.children_in_rank_order(parent, [0] * len(parent))
+    out = []
+
+    def rec(u, path):
+        if not kids[u]:
+            out.append(path)
+        for c in kids[u]:
+            rec(c, path + [c])
+    rec(0, [0])
+    return out
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_greedy_brute_force_longest_matching_path(seed):
+    rng = np.random.default_rng(seed)
+    V = 6
+    parent, rank = synth.random_tree(25, (4, 3, 3, 2), seed)
+    T = len(parent)
+    toks = np.zeros(T, np.int64)
+    for u, kids in enumerate(tree.children_in_rank_order(parent, rank)):
+        if kids:
+            toks[kids] = rng.choice(V, size=len(kids), replace=False)
+    base = rng.normal(size=(T, V))
+    # plant agreement along random edges so that long paths occur
+    for n in range(1, T):
+        if rng.random() < 0.5:
+            base[parent[n], toks[n]] += 10 * rng.random()
+    r = accept.accept_greedy(base, toks, parent, rank)
+    best = []
+    for path in _paths(parent):
+        k = 0
+        while k + 1 < len(path) and toks[path[k + 1]] == np.argmax(base[path[k]]):
+            k += 1
+        if k > len(best) - 1:
+            best = path[:k + 1]
+    assert r.nodes == best
+    assert r.tokens == [int(toks[n]) for n in best[1:]] + [int(np.argmax(base[best[-1]]))]
+
+
+def _toy_target_logits(prefix, V):
+    """Deterministic 'target model': logits are a seeded hash of the prefix."""
+    seed = hash(tuple(int(t) for t in prefix)) % (2 ** 32)
+    return np.random.default_rng(seed).normal(size=V)
+
+
+def test_greedy_speculation_equals_target_greedy():
+    """Multi-step greedy Medusa (oracle acceptance on trees of random
+    candidates) emits exactly the target's own greedy sequence."""
+    V = 5
+    rng = np.random.default_rng(0)
+    parent, rank = synth.cost_ordered_tree((3, 3, 2, 2), 16)
+    kids = tree.children_in_rank_order(parent, rank)
+    prompt = [1, 3]
+    n_tokens = 120
+    # target-only greedy
+    ref = list(prompt)
+    while len(ref) < len(prompt) + n_tokens:
+        ref.append(int(np.argmax(_toy_target_logits(ref, V))))
+    # speculative: root = the token decided last step; candidates are random
+    seq = list(prompt)
+    seq.append(int(np.argmax(_toy_target_logits(seq, V))))     # first root
+    steps = 0
+    while len(seq) < len(prompt) + n_tokens:
+        T = len(parent)
+        toks = np.zeros(T, np.int64)
+        toks[0] = seq[-1]
+        for u in range(T):
+            if kids[u]:
+                toks[kids[u]] = rng.choice(V, size=len(kids[u]), replace=False)
+        # base logits at node u: target logits after seq + path(root..u) minus root
+        base = np.zeros((T, V))
+        for u in range(T):
+            path, x = [], u
+            while x > 0:
+                path.append(int(toks[x]))
+                x = parent[x]
+            base[u] = _toy_target_logits(seq + path[::-1], V)
+        r = accept.accept_greedy(base, toks, parent, rank)
+        seq.extend(r.tokens)
+        steps += 1
+    assert seq[:len(ref)] == ref
+    assert steps < n_tokens          # speculation did accept something
+
+
+# ---------------------------------------------------------------------------
+# rejection sampling
+# ---------------------------------------------------------------------------
+
+def _sample_from(p, rng):
+    return int(rng.choice(len(p), p=p))
+
+
+def _one_step(parent, rank, tau, logp_at_node, logq_depth, rng, toks_fn):
+    """Run the oracle once on a tree whose drafts are sampled from q."""
+    T = len(parent)
+    toks = toks_fn(rng)
+    base = np.stack([logp_at_node(u, toks) for u in range(T)])
+    head = np.stack(logq_depth)
+    return accept.accept_rejection(base, head, toks, parent, rank,
+                                   rng.random(T), rng.random(T), tau)
+
+
+def test_single_draft_tvd_within_page_tolerance(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "p3_sampler_checks.json")))["tvd"]
+    rng = np.random.default_rng(10)
+    V = 8
+    p = rng.dirichlet(np.ones(V))
+    q = rng.dirichlet(np.ones(V))
+    parent, rank = synth.chain_tree(1)
+    n = g["samples"]
+    counts = np.zeros(V)
+    base = np.stack([np.log(p), np.zeros(V)])
+    head = np.log(q)[None]
+    xs = rng.choice(V, size=n, p=q)
+    ua = rng.random(n)
+    us = rng.random(n)
+    for i in range(n):
+        r = accept.accept_rejection(base, head, np.array([0, xs[i]]), parent, rank,
+                                    [0.0, ua[i]], [us[i], 0.0], 1.0)
+        counts[r.tokens[0]] += 1
+    tvd = 0.5 * np.abs(counts / n - p).sum()
+    assert tvd < g["tolerance"]
+    assert stats.chisquare(counts, n * p).pvalue > 1e-3
+
+
+def test_single_draft_acceptance_probability_is_sum_min():
+    """P(accept) = sum_x q(x) min(1, p(x)/q(x)) = sum_x min(p(x), q(x))."""
+    rng = np.random.default_rng(11)
+    V = 6
+    p = rng.dirichlet(np.ones(V))
+    q = rng.dirichlet(np.ones(V))
+    parent, rank = synth.chain_tree(1)
+    base = np.stack([np.log(p), np.zeros(V)])
+    n = 40000
+    acc = 0
+    for i in range(n):
+        x = _sample_from(q, rng)
+        r = accept.accept_rejection(base, np.log(q)[None], np.array([0, x]), parent, rank,
+                                    [0.0, rng.random()], [rng.random(), 0.0], 1.0)
+        acc += r.accept_len
+    expect = np.minimum(p, q).sum()
+    assert abs(acc / n - expect) < 4.5 * np.sqrt(expect * (1 - expect) / n)
+
+
+@pytest.mark.parametrize("n_children", [1, 2, 3])
+def test_multi_draft_siblings_are_lossless(n_children):
+    """Root with n i.i.d. drafts from q tried in turn with residual updates:
+    the first emitted token is distributed as p (chi-squared)."""
+    rng = np.random.default_rng(20 + n_children)
+    V = 5
+    p = rng.dirichlet(np.ones(V) * 0.7)
+    q = rng.dirichlet(np.ones(V) * 0.7)
+    parent = np.array([-1] + [0] * n_children, np.int32)
+    rank = np.arange(n_children + 1, dtype=np.int32)
+    rank[0] = 0
+    rank[1:] = np.arange(n_children)
+    base = np.stack([np.log(p)] + [np.zeros(V)] * n_children)
+    n = 30000
+    counts = np.zeros(V)
+    for i in range(n):
+        toks = np.concatenate([[0], rng.choice(V, size=n_children, p=q)])
+        r = accept.accept_rejection(base, np.log(q)[None], toks, parent, rank,
+                                    rng.random(n_children + 1), rng.random(n_children + 1), 1.0)
+        counts[r.tokens[0]] += 1
+    assert stats.chisquare(counts, n * p).pvalue > 1e-3
+
+
+def test_two_level_chain_joint_distribution_is_target():
+    """Root -> depth-1 draft -> depth-2 draft, drafts from q1, q2.  The pair of
+    the first two emitted tokens (a short step is continued by plain sampling
+    from the target, as the next step would) is distributed as
+    p_root(y1) * p(y2 | y1)."""
+    rng = np.random.default_rng(30)
+    V = 4
+    p_root = rng.dirichlet(np.ones(V))
+    p_next = rng.dirichlet(np.ones(V), size=V)      # p(y2 | y1)
+    q1 = rng.dirichlet(np.ones(V))
+    q2 = rng.dirichlet(np.ones(V))
+    parent, rank = synth.chain_tree(2)
+    head = np.log(np.stack([q1, q2]))
+    n = 40000
+    counts = np.zeros((V, V))
+    for i in range(n):
+        x1 = _sample_from(q1, rng)
+        x2 = _sample_from(q2, rng)
+        toks = np.array([0, x1, x2])
+        base = np.stack([np.log(p_root), np.log(p_next[x1]), np.log(rng.dirichlet(np.ones(V)))])
+        r = accept.accept_rejection(base, head, toks, parent, rank,
+                                    rng.random(3), rng.random(3), 1.0)
+        y = r.tokens
+        if len(y) == 1:
+            y = y + [_sample_from(p_next[y[0]], rng)]
+        counts[y[0], y[1]] += 1
+    expect = p_root[:, None] * p_next
+    assert stats.chisquare(counts.ravel(), n * expect.ravel()).pvalue > 1e-3
+
+
+def test_expected_tokens_closed_form(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "p3_sampler_checks.json")))["expected_tokens"]
+    e = accept.expected_tokens_per_step(g["alpha"], g["K"])
+    assert round(e, 4) == g["page_theory"]
+    # the page's simulated value sits within 1% of the formula
+    assert abs(g["page_simulated"] - e) / e < 0.01
+    # the sum form 1 + alpha + ... + alpha^K
+    assert e == pytest.approx(sum(g["alpha"] ** i for i in range(g["K"] + 1)), rel=1e-14)
+
+
+def test_expected_tokens_monte_carlo_constant_alpha(golden_dir):
+    """A K-deep chain where every draft is accepted with probability exactly
+    alpha (p and q fixed with sum(min(p, q)) = alpha, drafts from q): the mean
+    number of emitted tokens matches the closed form."""
+    g = json.load(open(os.path.join(golden_dir, "p3_sampler_checks.json")))["expected_tokens"]
+    alpha, K = g["alpha"], g["K"]
+    # p = (alpha, 1 - alpha, 0), q = (1, 0, 0) -> min sum = alpha
+    V = 3
+    p = np.array([alpha, 1 - alpha, 0.0])
+    q = np.array([1.0, 0.0, 0.0])
+    with np.errstate(divide="ignore"):
+        lp, lq = np.log(p), np.log(q)
+    parent, rank = synth.chain_tree(K)
+    base = np.stack([lp] * (K + 1))
+    head = np.stack([lq] * K)
+    toks = np.zeros(K + 1, np.int64)              # drafts from q are always token 0
+    rng = np.random.default_rng(40)
+    n = 20000
+    total = 0
+    for i in range(n):
+        r = accept.accept_rejection(base, head, toks, parent, rank,
+                                    rng.random(K + 1), rng.random(K + 1), 1.0)
+        total += len(r.tokens)
+        if r.accept_len < K:                      # a rejection resamples from the residual
+            assert r.tokens[-1] == 1
+    mean = total / n
+    e = accept.expected_tokens_per_step(alpha, K)
+    sd = np.sqrt(sum((j + 1) ** 2 * pj for j, pj in enumerate(
+        [alpha ** j * (1 - alpha) for j in range(K)] + [alpha ** K])) - e ** 2)
+    assert abs(mean - e) < 4.5 * sd / np.sqrt(n)
+
+
+def test_equal_distributions_always_accept():
+    rng = np.random.default_rng(50)
+    V = 7
+    z = rng.normal(size=V)
+    parent, rank = synth.cartesian_tree((2, 2))
+    T = len(parent)
+    for i in range(200):
+        toks = np.concatenate([[0], rng.choice(V, size=T - 1)])
+        r = accept.accept_rejection(np.stack([z] * T), np.stack([z, z]), toks, parent, rank,
+                                    rng.random(T), rng.random(T), 0.9)
+        assert r.accept_len == 2
+        assert r.nodes[1] == 1                     # first child in rank order accepted
+
+
+def test_disjoint_supports_always_reject():
+    V = 6
+    lp = np.log(np.array([0.5, 0.5, 0, 0, 0, 0]) + 1e-300)
+    lq = np.log(np.array([0, 0, 0.25, 0.25, 0.25, 0.25]) + 1e-300)
+    parent, rank = synth.cartesian_tree((3,))
+    rng = np.random.default_rng(51)
+    seen = set()
+    for i in range(300):
+        toks = np.array([0, 2, 3, 4])
+        r = accept.accept_rejection(np.stack([lp] * 4), lq[None], toks, parent, rank,
+                                    rng.random(4), rng.random(4), 1.0)
+        assert r.accept_len == 0
+        seen.add(r.tokens[0])
+    assert seen == {0, 1}
+
+
+def test_inverse_cdf_hand_values():
+    p = np.array([0.1, 0.2, 0.3, 0.4])
+    assert accept.inverse_cdf(p, 0.0)[0] == 0
+    assert accept.inverse_cdf(p, 0.05)[0] == 0
+    assert accept.inverse_cdf(p, 0.35)[0] == 2
+    assert accept.inverse_cdf(p, 0.999)[0] == 3
+    # zero-probability tokens are never drawn
+    p0 = np.array([0.0, 0.5, 0.0, 0.5])
+    assert accept.inverse_cdf(p0, 0.0)[0] == 1
+    assert accept.inverse_cdf(p0, 0.7)[0] == 3
+
+
+def test_temperature_scales_logits():
+    z = np.array([1.0, 2.0, 4.0])
+    np.testing.assert_allclose(accept.softmax_t(z, 0.5), np.exp(2 * z) / np.exp(2 * z).sum(),
+                               rtol=1e-14)
+
+
+def test_batched_padding():
+    w = synth.WORKLOADS["tiny-fp32"].scaled(B=3)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    toks = synth.tree_tokens_input(w, parent)
+    base, head, ua, us = [x.numpy() for x in synth.accept_inputs(w, parent, toks)]
+    acc, otok, onode, _ = accept.accept_paths(base, head, toks, parent, rank, ua, us, 1.0, w.K)
+    for b in range(3):
+        n = acc[b] + 1
+        assert np.all(otok[b, n:] == -1) and np.all(otok[b, :n] >= 0)
+        assert onode[b, 0] == 0 and np.all(onode[b, n:] == -1)
+
+
+def test_greedy_tie_takes_first_maximum():
+    """Equal top logits: the target's greedy pick is the lower token id (as
+    numpy's argmax reports), so the child carrying that token is accepted."""
+    parent, rank = synth.cartesian_tree((2,))
+    base = np.array([[0.0, 5.0, 5.0, 0.0], [0.0, 0.0, 0.0, 1.0], [1.0, 0.0, 0.0, 0.0]])
+    toks = np.array([3, 2, 1])                       # rank 0 carries token 2, rank 1 token 1
+    r = accept.accept_greedy(base, toks, parent, rank)
+    assert int(np.argmax(base[0])) == 1
+    assert r.nodes == [0, 2] and r.tokens == [1, 0]
