@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Medusa verify-step benchmark on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+medusa_heads -> medusa_tree_candidates -> medusa_tree_attention for every
+layer (each layer on its own Q/K/V buffers) -> medusa_accept_paths.  All
+inputs are resident in HBM before timing starts.  The step is captured once
+as a HIP graph and replayed (the host never sits in the timed loop); a second,
+eager pass records HIP events around every stage on the launch stream for the
+per-stage and per-kernel figures.
+
+Prints one JSON line (see the keys at the end of main()).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verify steps/sec + tree_attention HBM GB/s & head-GEMM MFMA % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="vicuna7b-shaped")
+    p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-layers", type=int, default=4,
+                   help="attention layers the CPU oracle runs (scaled to all layers)")
+    return p.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def attention_bytes(w) -> int:
+    """Algorithmic HBM bytes of one tree-attention layer: every K and V row of
+    every sequence's context + tree (read once), Q read and O written once."""
+    kv = w.B * w.Hkv * (w.ctx + w.T) * w.D * 2 * 2
+    qo = 2 * w.B * w.T * w.Hq * w.D * 2
+    return kv + qo
+
+
+def heads_bytes(w) -> int:
+    """Algorithmic HBM bytes of the heads: both weight matrices of every head
+    read once (bf16) plus hidden in, r round trip and fp32 logits out."""
+    weights = w.K * (w.H * w.H + w.H * w.V) * 2
+    acts = w.B * w.H * 2 + 2 * w.K * w.B * w.H * 2 + w.B * w.K * w.V * 4
+    return weights + acts
+
+
+def heads_flops(w) -> int:
+    return 2 * w.B * w.K * (w.H * w.H + w.H * w.V)
+
+
+def build_step(w, dev):
+    import torch
+    from medusa_tree_verification_amd import api, synth
+
+    log("generating inputs for", w.name)
+    hidden, w1, wlm = synth.head_inputs(w, dev)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    tree = api.Tree(parent, rank, w.topk)
+    root = synth.roots(w, dev)
+    ctx = torch.full((w.B,), w.ctx, dtype=torch.int32, device=dev)
+    layers = [synth.attention_inputs(w, l, dev)[:3] for l in range(w.L)]
+    base = synth.normal((w.B, w.T, w.V), w.base_logit_std, synth.seed_for(w.cfg_id, synth.T_BASE), dev)
+    ua = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_UACC), dev)
+    us = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_USMP), dev)
+
+    logits = torch.empty((w.B, w.K, w.V), dtype=torch.float32, device=dev)
+    topk = torch.empty((w.B, w.K, tree.kmax), dtype=torch.int32, device=dev)
+    toks = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
+    pos = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
+    outs = [torch.empty((w.B, w.T, w.Hq, w.D), dtype=torch.bfloat16, device=dev) for _ in range(w.L)]
+    acc_outs = {tau: (torch.empty(w.B, dtype=torch.int32, device=dev),
+                      torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev),
+                      torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev))
+                for tau in w.temperature}
+
+    def ws(n):
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+
+    ws_heads = ws(api.heads_workspace_size(w.B, w.H, w.K, torch.bfloat16))
+    ws_attn = ws(api.tree_attention_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.ctx, tree, torch.bfloat16))
+    ws_acc = ws(max(api.accept_workspace_size(w.B, w.V, tree, t) for t in w.temperature))
+
+    def stage_heads():
+        api.heads(hidden, w1, wlm, logits=logits, ws=ws_heads)
+
+    def stage_candidates():
+        api.tree_candidates(logits, root, ctx, tree, topk, toks, pos)
+
+    def stage_attention(l):
+        q, k, v = layers[l]
+        api.tree_attention(q, k, v, ctx, w.ctx, tree, out=outs[l], ws=ws_attn)
+
+    def stage_accept():
+        for tau, o in acc_outs.items():
+            api.accept_paths(base, logits, toks, tree, ua, us, tau, outs=o, ws=ws_acc)
+
+    def step():
+        stage_heads()
+        stage_candidates()
+        for l in range(w.L):
+            stage_attention(l)
+        stage_accept()
+
+    keep = dict(hidden=hidden, w1=w1, wlm=wlm, tree=tree, layers=layers, base=base)
+    return step, (stage_heads, stage_candidates, stage_attention, stage_accept), keep
+
+
+def time_gpu(w, args):
+    import torch
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    step, stages, keep = build_step(w, dev)
+    torch.cuda.synchronize()
+
+    run = step
+    if not args.eager:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(2):
+                step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        run = g.replay
+
+    log(f"warmup {args.warmup}, timing {args.steps} steps ({'eager' if args.eager else 'graph'})")
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # instrumented eager pass: events on the launch stream around every stage
+    stage_heads, stage_candidates, stage_attention, stage_accept = stages
+    names = ["heads", "candidates", "attention", "accept"]
+    acc = {n: 0.0 for n in names}
+    attn_calls = 0
+    reps = max(3, min(args.steps, 20))
+    for _ in range(reps):
+        ev = []
+
+        def mark():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            ev.append(e)
+
+        mark(); stage_heads(); mark(); stage_candidates(); mark()
+        attn_marks = []
+        for l in range(w.L):
+            stage_attention(l)
+            mark()
+            attn_marks.append(len(ev) - 1)
+        stage_accept(); mark()
+        torch.cuda.synchronize()
+        acc["heads"] += ev[0].elapsed_time(ev[1])
+        acc["candidates"] += ev[1].elapsed_time(ev[2])
+        prev = 2
+        for i in attn_marks:
+            acc["attention"] += ev[prev].elapsed_time(ev[i])
+            prev = i
+            attn_calls += 1
+        acc["accept"] += ev[prev].elapsed_time(ev[-1])
+    stages_us = {n: 1000.0 * acc[n] / reps for n in names}
+    attn_call_us = 1000.0 * acc["attention"] / attn_calls
+    return ms_per_step, wall_s, stages_us, attn_call_us
+
+
+def cpu_baseline(w, n_layers):
+    """The oracle as it stands (NumPy, fp64) on the host cores, on one step of
+    the same workload with attention run for n_layers layers and scaled to all
+    L layers."""
+    import numpy as np
+    import torch
+    from medusa_tree_verification_amd import synth
+    from oracle import accept as oaccept
+    from oracle import attention as oattn
+    from oracle import heads as oheads
+    from oracle import topk as otopk
+    from oracle import tree as otree
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    hidden, w1, wlm = synth.head_inputs(w, "cpu")
+    f64 = lambda t: t.to(torch.float64).numpy()
+    t0 = time.perf_counter()
+    logits = oheads.medusa_heads(f64(hidden), f64(w1), f64(wlm), round_r=w.dtype == "bf16")
+    t_heads = time.perf_counter() - t0
+    del w1, wlm
+    t0 = time.perf_counter()
+    tk = otopk.head_topk(logits, w.topk)
+    toks = otree.tree_tokens(tk, synth.roots(w, "cpu").numpy(), parent, rank)
+    vis = otree.visible_bruteforce(parent)
+    t_cand = time.perf_counter() - t0
+    t_attn = 0.0
+    for l in range(n_layers):
+        q, k, v, ctx = synth.attention_inputs(w, l, "cpu")
+        qd, kd, vd = f64(q), f64(k), f64(v)
+        t0 = time.perf_counter()
+        oattn.tree_attention(qd, kd, vd, ctx.numpy(), vis)
+        t_attn += time.perf_counter() - t0
+    t_attn *= w.L / n_layers
+    base = synth.normal((w.B, w.T, w.V), w.base_logit_std, synth.seed_for(w.cfg_id, synth.T_BASE))
+    ua = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_UACC))
+    us = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_USMP))
+    t0 = time.perf_counter()
+    for tau in w.temperature:
+        oaccept.accept_paths(base.numpy(), logits, toks, parent, rank, ua.numpy(), us.numpy(),
+                             tau, w.K)
+    t_acc = time.perf_counter() - t0
+    total = t_heads + t_cand + t_attn + t_acc
+    return {
+        "value": 1.0 / total,
+        "unit": "verify steps/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"one {w.name} step: heads, top-k/tree, acceptance in full; tree attention "
+                   f"on {n_layers} of {w.L} layers, scaled x{w.L / n_layers:g} (fp64 NumPy)"),
+        "stage_s": {"heads": round(t_heads, 3), "candidates": round(t_cand, 3),
+                    "attention": round(t_attn, 3), "accept": round(t_acc, 3)},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path's multi-GPU "
+              "sharding is described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+    from medusa_tree_verification_amd import synth
+    w = synth.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        sys.exit("bench.py times the bf16 workloads")
+
+    ms, wall_s, stages_us, attn_us = time_gpu(w, args)
+    a_bytes = attention_bytes(w)
+    h_bytes = heads_bytes(w)
+    attn_gbs = a_bytes / (attn_us * 1e-6) / 1e9
+    heads_gbs = h_bytes / (stages_us["heads"] * 1e-6) / 1e9
+    heads_tflops = heads_flops(w) / (stages_us["heads"] * 1e-6) / 1e12
+    attn_total = stages_us["attention"]
+    dominant_attention = attn_total >= stages_us["heads"]
+    if dominant_attention:
+        roof = {"kernel": "tree_attn_bf16 (+ split merge), one layer", "bound": "hbm",
+                "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": a_bytes, "us_per_launch": round(attn_us, 2)}
+    else:
+        roof = {"kernel": "skinny_gemm_bf16 x2 (residual block + vocab projection)", "bound": "hbm",
+                "achieved": round(heads_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(heads_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": h_bytes, "us_per_launch": round(stages_us["heads"], 2)}
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms, 2),
+        "unit": "verify steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "hidden": w.H, "vocab": w.V, "heads": w.K,
+                   "tree_nodes": w.T, "topk": list(w.topk), "layers": w.L, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.D, "context": w.ctx,
+                   "acceptance": ["greedy" if t == 0 else f"rejection tau={t}" for t in w.temperature],
+                   "timing": "eager" if args.eager else "hip graph replay"},
+        "roofline": roof,
+        "tree_attention_hbm_gbs": round(attn_gbs, 1),
+        "heads": {"hbm_gbs": round(heads_gbs, 1), "hbm_frac": round(heads_gbs / HBM_PEAK_GBS, 4),
+                  "mfma_tflops": round(heads_tflops, 2),
+                  "mfma_frac": round(heads_tflops / BF16_MFMA_PEAK_TFLOPS, 5)},
+        "stages_us": {k: round(v, 2) for k, v in stages_us.items()},
+        "wall_s_timed": round(wall_s, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_layers)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

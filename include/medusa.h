@@ -1,0 +1,245 @@
+/*
+ * medusa.h -- C ABI of the Medusa verify-step library for AMD Instinct MI355X
+ * (gfx950, wave64, CDNA4).
+ *
+ * One Medusa verify step has four stages, each one call here:
+ *   medusa_heads            K residual-SiLU heads + vocab projections
+ *   medusa_tree_candidates  per-head top-k, candidate tree tokens, positions
+ *   medusa_tree_attention   tree-masked attention of one layer (split-KV)
+ *   medusa_accept_paths     longest accepted root-to-leaf path (greedy or
+ *                           rejection sampling)
+ *
+ * Pages that define the operations (cited per call):
+ *   P1 "Medusa 심층 아키텍처: 별도 초안 모델을 제거한 다중 헤드(Multi-Head) 추측 디코딩과
+ *      Tree Attention 3배 가속 원리" (techknowgenie.com)
+ *   P2 "[vLLM] Medusa: 다중 예측 헤드 투기적 디코딩" (blog.secrett2633.cloud)
+ *   P3 "Speculative Decoding(투기적 디코딩) 원리와 가속 아키텍처 ..." (blog.huny.dev)
+ *   P4 "최적화 2편. 추측 디코딩과 긴 컨텍스트 - Speculative Decoding과 MEDUSA·EAGLE,
+ *      Ring Attention" (beengineer500.github.io)
+ *
+ * Conventions common to every call
+ *   - Tensor arguments are DEVICE pointers owned by the caller, on the
+ *     device that is current when the call is made, unless a parameter says
+ *     "host".  The library never keeps them after the call returns.
+ *   - Layouts are dense row-major in the order written ("[B][T][V]": V is
+ *     contiguous).  bf16 tensors are 16-bit bfloat16 bit patterns.
+ *   - Calls are asynchronous on the given stream (NULL = the null stream);
+ *     nothing synchronises the host.  Work is enqueued only after every
+ *     argument check passed.
+ *   - Return value: MEDUSA_OK or a negative MEDUSA_E* code; the reason is
+ *     in medusa_last_error() (thread-local, valid until the next call on the
+ *     same thread).  No exception crosses the ABI.
+ *   - Scratch memory is passed in by the caller (ws, ws_bytes, sized by the
+ *     matching *_workspace_size call, 256-byte aligned).  No call allocates
+ *     device memory except medusa_tree_create.
+ *   - Floating-point inputs must be finite.  Non-finite inputs give
+ *     unspecified outputs, but every kernel still terminates and every index
+ *     written stays in its documented range (or -1).
+ *   - Calls that share a workspace or output on one stream are ordered by
+ *     the stream; concurrent calls on different streams must not share them.
+ */
+#ifndef MEDUSA_H
+#define MEDUSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MEDUSA_OK            0
+#define MEDUSA_EINVAL       (-1) /* invalid argument: shape, range, NULL pointer */
+#define MEDUSA_EUNSUPPORTED (-2) /* valid but not implemented (e.g. a head dim) */
+#define MEDUSA_EWORKSPACE   (-3) /* workspace missing, misaligned or too small */
+#define MEDUSA_EHIP         (-4) /* a HIP runtime call or kernel launch failed */
+
+/* Limits of this implementation. */
+#define MEDUSA_MAX_TREE_NODES 256 /* T, root included */
+#define MEDUSA_MAX_HEADS       16 /* K */
+#define MEDUSA_MAX_TOPK        32 /* candidates kept per head */
+
+typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype_t;
+
+/* Opaque static tree (topology + ancestor bitmask), resident on one device. */
+typedef struct medusa_tree medusa_tree_t;
+
+/* Thread-local text of the last error on this thread ("" after success). */
+const char* medusa_last_error(void);
+
+/* Library version string, e.g. "medusa-amd 0.1 gfx950". */
+const char* medusa_version(void);
+
+/* ------------------------------------------------------------------------
+ * Static candidate tree
+ *
+ * P1, section "트리 어텐션 ... 고정 트리 토폴로지와 2차원 어텐션 마스크": head d
+ * contributes its top candidates at depth d and a fixed topology combines
+ * them into paths; token i may attend to tree token j iff j is an ancestor
+ * of i or j = i.  P1's sketch code ("build_tree_attention_mask") builds the
+ * mask by inheriting each parent's row, which needs parents before children.
+ *
+ * Topology (HOST arrays, length T):
+ *   parent[0] = -1 (node 0 is the root, the token already chosen by the base
+ *   model); for n >= 1, 0 <= parent[n] < n.
+ *   rank[n]   = which candidate of head depth(n) node n carries,
+ *               0 <= rank[n] < k_per_depth[depth(n)-1]; siblings need
+ *               distinct ranks.  rank[0] is ignored.
+ *   k_per_depth[K] = candidates kept by head d = 1..K (1..MEDUSA_MAX_TOPK).
+ *   depth(n) <= K, T <= MEDUSA_MAX_TREE_NODES, K <= MEDUSA_MAX_HEADS.
+ * Ancestor bitmask: W = ceil(T/64) uint64 words per node; bit (j % 64) of
+ * word j / 64 of row i is set iff j is an ancestor of i or j == i.
+ * ------------------------------------------------------------------------ */
+
+/* Host-only validation and mask construction (no GPU needed).
+ * mask_out: HOST [T][W] uint64 or NULL; depth_out: HOST [T] int32 or NULL.
+ * Returns MEDUSA_EINVAL (with the offending node in the message) for an
+ * invalid topology. */
+int medusa_tree_build_host(const int32_t* parent, const int32_t* rank, int T,
+                           const int32_t* k_per_depth, int K,
+                           uint64_t* mask_out, int32_t* depth_out);
+
+/* Validates the topology (as above), builds depth, rank-ordered child
+ * lists and the ancestor bitmask, and uploads them to the CURRENT device
+ * (one device allocation, synchronous).  *out receives a handle owned by the
+ * library; free it with medusa_tree_destroy.  The handle may only be used
+ * with the device that was current at creation (EINVAL otherwise). */
+int medusa_tree_create(const int32_t* parent, const int32_t* rank, int T,
+                       const int32_t* k_per_depth, int K, medusa_tree_t** out);
+
+/* Frees the handle and its device memory.  NULL is a no-op.  The caller
+ * must make sure no enqueued call still uses the tree. */
+void medusa_tree_destroy(medusa_tree_t* tree);
+
+/* Copies the ancestor bitmask to HOST memory host_out [T][W]. */
+int medusa_tree_mask(const medusa_tree_t* tree, uint64_t* host_out);
+
+/* Shape query; any output pointer may be NULL.  kmax = max(k_per_depth). */
+int medusa_tree_info(const medusa_tree_t* tree, int32_t* T, int32_t* K, int32_t* W,
+                     int32_t* max_depth, int32_t* kmax);
+
+/* ------------------------------------------------------------------------
+ * Stage 1+2: Medusa heads
+ *
+ * P1, section "Medusa의 핵심 철학 ... 잔차 블록을 포함한 Medusa 헤드 구조": head k
+ * maps the last hidden state h to r = SiLU(h W_res^(k)) + h and to logits
+ * r W_head^(k) (softmax is applied later, where probabilities are needed).
+ * P1's sketch code: both projections are bias-free [out, in] linear layers.
+ * W_head may be shared by all heads (P1 allows reusing the frozen base
+ * unembedding) -- pass wlm_head_stride = 0.
+ *
+ *   hidden  [M][H]                    dt
+ *   w1      head k at w1 + k*w1_head_stride elements, each [H][H] ([out][in]), dt
+ *   wlm     head k at wlm + k*wlm_head_stride elements, each [V][H], dt
+ *   logits  [M][K][V] fp32 (output)
+ * For dt = MEDUSA_BF16 the residual output r is rounded to bf16 (round to
+ * nearest even) before the vocab projection; accumulation is fp32.
+ * Constraints: M >= 1, K in 1..MEDUSA_MAX_HEADS, H % 8 == 0 (bf16) ,
+ * V >= 1, w1_head_stride >= H*H (or 0 only if K == 1), wlm_head_stride == 0
+ * or >= V*H.  Pointers 16-byte aligned.
+ * Workspace: holds r, K*M*H elements of dt.
+ * ------------------------------------------------------------------------ */
+size_t medusa_heads_workspace_size(int M, int H, int K, medusa_dtype_t dt);
+
+int medusa_heads(const void* hidden, const void* w1, int64_t w1_head_stride,
+                 const void* wlm, int64_t wlm_head_stride, int M, int H, int V, int K,
+                 medusa_dtype_t dt, float* logits, void* ws, size_t ws_bytes,
+                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 3+4: per-head top-k and candidate tree tokens
+ *
+ * P1, section "소스코드 레벨 구조 분석" (generate_candidates): each head keeps
+ * the indices of its k largest logits; P2, section "propose()": the k = 1
+ * case is the per-head argmax.  Order: descending logit, equal logits by
+ * ascending index.  Tree tokens: node 0 carries root[b]; node n carries
+ * candidate rank(n) of head depth(n).  Positions: ctx_len[b] + depth(n).
+ *
+ *   head_logits [B][K][V] fp32 (K = the tree's K)
+ *   root        [B] int32 (token t+1 from the base model)
+ *   ctx_len     [B] int32 (tokens already in the KV cache)
+ *   topk_idx    [B][K][kmax] int32 (output; -1 beyond head d's k_d)
+ *   tree_tokens [B][T] int32 (output)
+ *   pos         [B][T] int32 (output)
+ * ------------------------------------------------------------------------ */
+int medusa_tree_candidates(const float* head_logits, const int32_t* root,
+                           const int32_t* ctx_len, const medusa_tree_t* tree, int B, int V,
+                           int32_t* topk_idx, int32_t* tree_tokens, int32_t* pos,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 5: tree-masked attention (one layer)
+ *
+ * P1, section "트리 어텐션 ... 2차원 어텐션 마스크": all tree tokens are verified
+ * in one attention pass where tree token i sees the cached context and,
+ * among tree tokens, only its ancestors and itself.  P4, section 3.3: partial
+ * results over key blocks merge exactly through a running max and exp-sum,
+ * which is how the key range is split across workgroups here.
+ *
+ *   q       [B][T][Hq][D]        dt (already position-encoded)
+ *   k_cache [B][Hkv][S_cap][D]   dt; slots 0..ctx_len[b]-1 hold the context,
+ *   v_cache [B][Hkv][S_cap][D]   dt; slots ctx_len[b]+j hold tree token j
+ *   ctx_len [B] int32, 0 <= ctx_len[b] <= S_cap - T (values outside are
+ *           clamped into that range so that no access leaves the cache)
+ *   ctx_max HOST upper bound of ctx_len[] (sizes the split grid; a larger
+ *           ctx_len still gives the right result, only slower)
+ *   out     [B][T][Hq][D]        dt
+ * Query head h uses K/V head h / (Hq/Hkv).  softmax(scale * q.k) with fp32
+ * scores, sums and accumulators; bf16 operands use MFMA.
+ * Constraints: Hq % Hkv == 0; D = 128 (bf16) or D <= 128, D % 4 == 0 (f32);
+ * T = the tree's T; S_cap >= ctx_max + T.  Pointers 16-byte aligned.
+ * Workspace: split partials (see medusa_tree_attention_workspace_size).
+ * ------------------------------------------------------------------------ */
+size_t medusa_tree_attention_workspace_size(int B, int Hq, int Hkv, int D, int ctx_max,
+                                            const medusa_tree_t* tree, medusa_dtype_t dt);
+
+int medusa_tree_attention(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* ctx_len, int ctx_max, const medusa_tree_t* tree,
+                          int B, int Hq, int Hkv, int D, int S_cap, float scale,
+                          medusa_dtype_t dt, void* out, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 6: path acceptance
+ *
+ * temperature == 0: greedy.  P3, section 5 (greedy check) and P4, section
+ * 1.3: walk from the root; at node u take the target's argmax t* of
+ * base_logits[b][u] (first maximum); if a child of u carries t* (lowest rank
+ * if several), move there, else stop.  The step emits the accepted nodes'
+ * tokens and then t* (the correction, or the bonus token at a leaf).
+ *
+ * temperature > 0: rejection sampling.  P1, section "수학적 무손실 보장: 기각
+ * 샘플링": a draft x is accepted iff u < min(1, p(x)/q(x)); after a rejection
+ * p becomes max(0, p - q) / sum(max(0, p - q)); P3, section 2, shows the
+ * output is distributed as p.  On the tree: p_u = softmax(base_logits[b][u]
+ * / temperature), q_d = softmax(head_logits[b][d-1] / temperature) for a child
+ * at depth d; children are tried in rank order with u_accept[b][child]; a
+ * rejection turns p into the residual before the next sibling; an accepted
+ * child becomes the current node; at a leaf or after rejecting every child,
+ * one token is drawn from the current p by inverse CDF with u_sample[b][u]
+ * (smallest v with cumsum(p)[v] > u * sum(p)).  Probabilities are fp64.
+ *
+ *   base_logits [B][T][V] fp32   target logits after each tree node
+ *   head_logits [B][K][V] fp32   (rejection only; NULL allowed for greedy)
+ *   tree_tokens [B][T] int32
+ *   u_accept, u_sample [B][T] fp32 in [0, 1) (rejection only; may be NULL for greedy)
+ *   accept_len  [B] int32 (output) number of accepted tree nodes, 0..max depth
+ *   out_tokens  [B][K+1] int32 (output) accept_len + 1 emitted tokens, -1 after
+ *   out_nodes   [B][K+1] int32 (output) root (0) then the accepted nodes, -1 after
+ * Workspace: rejection sampling keeps one fp64 distribution per sequence.
+ * ------------------------------------------------------------------------ */
+size_t medusa_accept_workspace_size(int B, int V, const medusa_tree_t* tree,
+                                    float temperature);
+
+int medusa_accept_paths(const float* base_logits, const float* head_logits,
+                        const int32_t* tree_tokens, const medusa_tree_t* tree,
+                        const float* u_accept, const float* u_sample, float temperature,
+                        int B, int V, int32_t* accept_len, int32_t* out_tokens,
+                        int32_t* out_nodes, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEDUSA_H */

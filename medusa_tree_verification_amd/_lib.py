@@ -1,0 +1,62 @@
+"""ctypes declarations of the C ABI in include/medusa.h.
+
+Loading fails loudly (RuntimeError) when the built library is absent: there
+is no fallback implementation of any stage.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_NAME = "libmedusa_amd.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+c_int, c_int32, c_int64, c_size_t, c_float, c_void_p = (
+    ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p)
+P_i32 = ctypes.POINTER(ctypes.c_int32)
+P_u64 = ctypes.POINTER(ctypes.c_uint64)
+P_void = ctypes.c_void_p
+
+# name -> (restype, argtypes); mirrors include/medusa.h
+SIGNATURES = {
+    "medusa_last_error": (ctypes.c_char_p, []),
+    "medusa_version": (ctypes.c_char_p, []),
+    "medusa_tree_build_host": (c_int, [P_i32, P_i32, c_int, P_i32, c_int, P_u64, P_i32]),
+    "medusa_tree_create": (c_int, [P_i32, P_i32, c_int, P_i32, c_int, ctypes.POINTER(c_void_p)]),
+    "medusa_tree_destroy": (None, [c_void_p]),
+    "medusa_tree_mask": (c_int, [c_void_p, P_u64]),
+    "medusa_tree_info": (c_int, [c_void_p, P_i32, P_i32, P_i32, P_i32, P_i32]),
+    "medusa_heads_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "medusa_heads": (c_int, [P_void, P_void, c_int64, P_void, c_int64, c_int, c_int, c_int, c_int,
+                             c_int, P_void, P_void, c_size_t, P_void]),
+    "medusa_tree_candidates": (c_int, [P_void, P_void, P_void, c_void_p, c_int, c_int, P_void,
+                                       P_void, P_void, P_void]),
+    "medusa_tree_attention_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int,
+                                                        c_void_p, c_int]),
+    "medusa_tree_attention": (c_int, [P_void, P_void, P_void, P_void, c_int, c_void_p, c_int,
+                                      c_int, c_int, c_int, c_int, c_float, c_int, P_void, P_void,
+                                      c_size_t, P_void]),
+    "medusa_accept_workspace_size": (c_size_t, [c_int, c_int, c_void_p, c_float]),
+    "medusa_accept_paths": (c_int, [P_void, P_void, P_void, c_void_p, P_void, P_void, c_float,
+                                    c_int, c_int, P_void, P_void, P_void, P_void, c_size_t,
+                                    P_void]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """The library handle, loaded once.  Raises RuntimeError if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_NAME} is not built (expected at {LIB_PATH}); run __graft_entry__.build() "
+                "or python medusa_tree_verification_amd/build.py")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib

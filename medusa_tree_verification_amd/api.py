@@ -1,0 +1,207 @@
+"""Python binding of the Medusa verify-step library (argument marshalling only).
+
+Tensors are torch tensors on the current HIP device (torch supplies device
+memory and the stream); every stage runs in the HIP library.  Each function
+has the name of its C entry point without the ``medusa_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+_CODES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EWORKSPACE: "EWORKSPACE", EHIP: "EHIP"}
+
+
+class MedusaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise MedusaError(rc, _lib.load().medusa_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _p32(a: np.ndarray):
+    return a.ctypes.data_as(_lib.P_i32)
+
+
+def version() -> str:
+    return _lib.load().medusa_version().decode()
+
+
+def tree_build_host(parent, rank, k_per_depth):
+    """Host-only validation + ancestor bitmask: returns (mask [T][W] uint64, depth [T])."""
+    lib = _lib.load()
+    parent, rank, kpd = _i32(parent), _i32(rank), _i32(k_per_depth)
+    T = len(parent)
+    W = (T + 63) // 64
+    mask = np.zeros((T, W), np.uint64)
+    depth = np.zeros(T, np.int32)
+    _check(lib.medusa_tree_build_host(_p32(parent), _p32(rank), T, _p32(kpd), len(kpd),
+                                      mask.ctypes.data_as(_lib.P_u64), _p32(depth)))
+    return mask, depth
+
+
+class Tree:
+    """A static candidate tree resident on the current device."""
+
+    def __init__(self, parent, rank, k_per_depth):
+        lib = _lib.load()
+        self._lib = lib
+        self.parent, self.rank, self.k_per_depth = _i32(parent), _i32(rank), _i32(k_per_depth)
+        h = ctypes.c_void_p()
+        _check(lib.medusa_tree_create(_p32(self.parent), _p32(self.rank), len(self.parent),
+                                      _p32(self.k_per_depth), len(self.k_per_depth),
+                                      ctypes.byref(h)))
+        self.handle = h
+        vals = [ctypes.c_int32() for _ in range(5)]
+        _check(lib.medusa_tree_info(h, *[ctypes.byref(v) for v in vals]))
+        self.T, self.K, self.W, self.max_depth, self.kmax = [v.value for v in vals]
+
+    def mask(self) -> np.ndarray:
+        out = np.zeros((self.T, self.W), np.uint64)
+        _check(self._lib.medusa_tree_mask(self.handle, out.ctypes.data_as(_lib.P_u64)))
+        return out
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            self._lib.medusa_tree_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return ws, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def heads_workspace_size(M: int, H: int, K: int, dtype: torch.dtype) -> int:
+    return _lib.load().medusa_heads_workspace_size(M, H, K, F32 if dtype == torch.float32 else BF16)
+
+
+def heads(hidden: torch.Tensor, w1: torch.Tensor, wlm: torch.Tensor, logits=None, ws=None,
+          stream=None) -> torch.Tensor:
+    """hidden [M,H]; w1 [K,H,H]; wlm [K,V,H] or [V,H] (shared) -> logits [M,K,V] fp32."""
+    lib = _lib.load()
+    M, H = hidden.shape
+    K = w1.shape[0]
+    shared = wlm.dim() == 2
+    V = wlm.shape[0] if shared else wlm.shape[1]
+    if logits is None:
+        logits = torch.empty((M, K, V), dtype=torch.float32, device=hidden.device)
+    dt = _dt(hidden)
+    ws, nb = _workspace(lib.medusa_heads_workspace_size(M, H, K, dt), hidden.device, ws)
+    _check(lib.medusa_heads(_ptr(hidden), _ptr(w1), H * H, _ptr(wlm), 0 if shared else V * H,
+                            M, H, V, K, dt, _ptr(logits), _ptr(ws), nb, _stream(stream)))
+    return logits
+
+
+def tree_candidates(head_logits: torch.Tensor, root: torch.Tensor, ctx_len: torch.Tensor,
+                    tree: Tree, topk_idx=None, tree_tokens=None, pos=None, stream=None):
+    """head_logits [B,K,V] fp32 -> (topk_idx [B,K,kmax], tree_tokens [B,T], pos [B,T]) int32."""
+    lib = _lib.load()
+    B, K, V = head_logits.shape
+    dev = head_logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty((B, tree.K, tree.kmax), dtype=torch.int32, device=dev)
+    if tree_tokens is None:
+        tree_tokens = torch.empty((B, tree.T), dtype=torch.int32, device=dev)
+    if pos is None:
+        pos = torch.empty((B, tree.T), dtype=torch.int32, device=dev)
+    _check(lib.medusa_tree_candidates(_ptr(head_logits), _ptr(root), _ptr(ctx_len), tree.handle, B,
+                                      V, _ptr(topk_idx), _ptr(tree_tokens), _ptr(pos),
+                                      _stream(stream)))
+    return topk_idx, tree_tokens, pos
+
+
+def tree_attention_workspace_size(B, Hq, Hkv, D, ctx_max, tree: Tree, dtype) -> int:
+    return _lib.load().medusa_tree_attention_workspace_size(
+        B, Hq, Hkv, D, ctx_max, tree.handle, F32 if dtype == torch.float32 else BF16)
+
+
+def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   ctx_len: torch.Tensor, ctx_max: int, tree: Tree, scale: Optional[float] = None,
+                   out=None, ws=None, stream=None) -> torch.Tensor:
+    """q [B,T,Hq,D]; k_cache/v_cache [B,Hkv,S_cap,D] -> out [B,T,Hq,D]."""
+    lib = _lib.load()
+    B, T, Hq, D = q.shape
+    Hkv, S_cap = k_cache.shape[1], k_cache.shape[2]
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = lib.medusa_tree_attention_workspace_size(B, Hq, Hkv, D, ctx_max, tree.handle, dt)
+    ws, nb = _workspace(nbytes, q.device, ws)
+    _check(lib.medusa_tree_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), ctx_max,
+                                     tree.handle, B, Hq, Hkv, D, S_cap, float(scale), dt, _ptr(out),
+                                     _ptr(ws), nb, _stream(stream)))
+    return out
+
+
+def accept_workspace_size(B, V, tree: Tree, temperature: float) -> int:
+    return _lib.load().medusa_accept_workspace_size(B, V, tree.handle, float(temperature))
+
+
+def accept_paths(base_logits: torch.Tensor, head_logits: Optional[torch.Tensor],
+                 tree_tokens: torch.Tensor, tree: Tree, u_accept: Optional[torch.Tensor],
+                 u_sample: Optional[torch.Tensor], temperature: float, outs=None, ws=None,
+                 stream=None):
+    """-> (accept_len [B], out_tokens [B,K+1], out_nodes [B,K+1]) int32."""
+    lib = _lib.load()
+    B, T, V = base_logits.shape
+    dev = base_logits.device
+    if outs is None:
+        outs = (torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty((B, tree.K + 1), dtype=torch.int32, device=dev),
+                torch.empty((B, tree.K + 1), dtype=torch.int32, device=dev))
+    acc, toks, nodes = outs
+    ws, nb = _workspace(lib.medusa_accept_workspace_size(B, V, tree.handle, float(temperature)),
+                        dev, ws)
+    _check(lib.medusa_accept_paths(_ptr(base_logits), _ptr(head_logits), _ptr(tree_tokens),
+                                   tree.handle, _ptr(u_accept), _ptr(u_sample), float(temperature),
+                                   B, V, _ptr(acc), _ptr(toks), _ptr(nodes), _ptr(ws), nb,
+                                   _stream(stream)))
+    return acc, toks, nodes

@@ -1,0 +1,382 @@
+// Path acceptance: greedy match or rejection sampling over the static tree.
+//
+// Greedy follows P3 ("Speculative Decoding(투기적 디코딩) 원리와 가속 아키텍처"),
+// section 5 (greedy check): drafts are compared with the target's argmax and
+// the first mismatch is replaced by it; P4 ("추측 디코딩과 긴 컨텍스트"), section
+// 1.3: everything after the first mismatch is dropped and, when every draft
+// matches, the target's next prediction is a free extra token.
+//
+// Rejection sampling follows P1 ("Medusa 심층 아키텍처"), section "수학적 무손실
+// 보장: 기각 샘플링": a draft x is accepted iff r < min(1, p(x)/q(x)); after a
+// rejection the target distribution is replaced by the residual
+// max(0, p - q) / sum(max(0, p - q)); P3, section 2, proves the emitted token
+// is distributed as p.  On the tree the children of the current node are
+// tried in rank order (the residual carries over from one sibling to the
+// next), an accepted child becomes the current node, and the walk ends with
+// one token drawn from the current p by inverse CDF.
+//
+// One workgroup per sequence.  The walk is sequential by nature; each step
+// is a block-wide pass over the vocabulary.  Probabilities are fp64 so that
+// the accept/reject decisions and the sampled token agree with an fp64
+// reference except in ties at the 1e-12 level.
+#include "internal.h"
+
+using namespace medusa;
+
+namespace {
+
+__device__ __forceinline__ bool beats(float v, int i, float w, int j) {
+  return v > w || (v == w && static_cast<unsigned>(i) < static_cast<unsigned>(j));
+}
+
+struct AcceptArgs {
+  const float* base;   // [B][T][V]
+  const float* head;   // [B][K][V]
+  const int32_t* toks; // [B][T]
+  const float* ua;     // [B][T]
+  const float* us;     // [B][T]
+  const int32_t* child_start;
+  const int32_t* child_list;
+  const int32_t* depth;
+  int T, V, K, Kp1, max_depth;
+  float tau;
+  int32_t* acc_len;
+  int32_t* out_tokens;
+  int32_t* out_nodes;
+  double* pbuf;        // [B][V]
+};
+
+// ---------------------------------------------------------------------------
+// greedy
+// ---------------------------------------------------------------------------
+constexpr int GT = 256;
+
+__global__ __launch_bounds__(GT) void accept_greedy_kernel(AcceptArgs a) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_v[GT / 64];
+  __shared__ int s_i[GT / 64];
+  __shared__ int s_next, s_tok;
+  int u = 0, len = 0, t = -1;
+  int32_t* onodes = a.out_nodes + static_cast<int64_t>(b) * a.Kp1;
+  int32_t* otoks = a.out_tokens + static_cast<int64_t>(b) * a.Kp1;
+  for (int iter = 0; iter <= a.max_depth; ++iter) {
+    const float* row = a.base + (static_cast<int64_t>(b) * a.T + u) * a.V;
+    float bv = -INFINITY;
+    int bi = -1;
+    int v = tid;
+    for (; v + 7 * GT < a.V; v += 8 * GT) {
+      float buf[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) buf[k] = row[v + k * GT];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (beats(buf[k], v + k * GT, bv, bi)) {
+          bv = buf[k];
+          bi = v + k * GT;
+        }
+    }
+    for (; v < a.V; v += GT)
+      if (beats(row[v], v, bv, bi)) {
+        bv = row[v];
+        bi = v;
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      float ov = __shfl_xor(bv, off, 64);
+      int oi = __shfl_xor(bi, off, 64);
+      if (beats(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      s_v[wave] = bv;
+      s_i[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float wv = s_v[0];
+      int wi = s_i[0];
+      for (int w = 1; w < GT / 64; ++w)
+        if (beats(s_v[w], s_i[w], wv, wi)) {
+          wv = s_v[w];
+          wi = s_i[w];
+        }
+      int nxt = -1;
+      for (int ci = a.child_start[u]; ci < a.child_start[u + 1]; ++ci) {
+        const int c = a.child_list[ci];
+        if (a.toks[static_cast<int64_t>(b) * a.T + c] == wi) {
+          nxt = c;
+          break;
+        }
+      }
+      s_tok = wi;
+      s_next = nxt;
+      onodes[len] = u;
+    }
+    __syncthreads();
+    t = s_tok;
+    const int nxt = s_next;
+    __syncthreads();  // s_* are rewritten next iteration
+    if (nxt < 0) break;
+    if (tid == 0) otoks[len] = a.toks[static_cast<int64_t>(b) * a.T + nxt];
+    ++len;
+    u = nxt;
+  }
+  if (tid == 0) {
+    otoks[len] = t;
+    a.acc_len[b] = len;
+    for (int j = len + 1; j < a.Kp1; ++j) {
+      otoks[j] = -1;
+      onodes[j] = -1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rejection sampling (fp64)
+// ---------------------------------------------------------------------------
+constexpr int RT = 1024;
+constexpr int RW = RT / 64;
+
+__device__ double block_sum(double x, double* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  __syncthreads();
+  if (lane == 0) sh[wave] = x;
+  __syncthreads();
+  double s = 0.0;
+  for (int w = 0; w < RW; ++w) s += sh[w];  // same order in every thread
+  return s;
+}
+
+__device__ double block_max(double x, double* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmax(x, __shfl_xor(x, off, 64));
+  __syncthreads();
+  if (lane == 0) sh[wave] = x;
+  __syncthreads();
+  double m = sh[0];
+  for (int w = 1; w < RW; ++w) m = fmax(m, sh[w]);
+  return m;
+}
+
+__device__ int block_min_int(int x, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = min(x, __shfl_xor(x, off, 64));
+  __syncthreads();
+  if (lane == 0) sh[wave] = x;
+  __syncthreads();
+  int m = sh[0];
+  for (int w = 1; w < RW; ++w) m = min(m, sh[w]);
+  return m;
+}
+
+__device__ int block_max_int(int x, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
+  __syncthreads();
+  if (lane == 0) sh[wave] = x;
+  __syncthreads();
+  int m = sh[0];
+  for (int w = 1; w < RW; ++w) m = max(m, sh[w]);
+  return m;
+}
+
+// p <- softmax(z / tau), fp64, written to p[0..V)
+__device__ void softmax_into(const float* z, double tau, int V, double* p, double* shd) {
+  double mx = -INFINITY;
+  for (int v = threadIdx.x; v < V; v += RT) mx = fmax(mx, static_cast<double>(z[v]) / tau);
+  mx = block_max(mx, shd);
+  double s = 0.0;
+  for (int v = threadIdx.x; v < V; v += RT) {
+    const double e = exp(static_cast<double>(z[v]) / tau - mx);
+    p[v] = e;
+    s += e;
+  }
+  const double Z = block_sum(s, shd);
+  for (int v = threadIdx.x; v < V; v += RT) p[v] = p[v] / Z;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(RT) void accept_reject_kernel(AcceptArgs a) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ double shd[RW];
+  __shared__ int shi[RW];
+  __shared__ double s_mq[MEDUSA_MAX_HEADS + 1], s_zq[MEDUSA_MAX_HEADS + 1];
+  const double tau = static_cast<double>(a.tau);
+  const int V = a.V;
+  double* p = a.pbuf + static_cast<int64_t>(b) * V;
+  const float* hb = a.head + static_cast<int64_t>(b) * a.K * V;
+  const int32_t* tk = a.toks + static_cast<int64_t>(b) * a.T;
+
+  // q_d = softmax(head[d-1] / tau): keep its max and normaliser per depth
+  for (int d = 1; d <= a.max_depth; ++d) {
+    const float* h = hb + static_cast<int64_t>(d - 1) * V;
+    double mx = -INFINITY;
+    for (int v = tid; v < V; v += RT) mx = fmax(mx, static_cast<double>(h[v]) / tau);
+    mx = block_max(mx, shd);
+    double s = 0.0;
+    for (int v = tid; v < V; v += RT) s += exp(static_cast<double>(h[v]) / tau - mx);
+    s = block_sum(s, shd);
+    if (tid == 0) {
+      s_mq[d] = mx;
+      s_zq[d] = s;
+    }
+  }
+  __syncthreads();
+
+  softmax_into(a.base + static_cast<int64_t>(b) * a.T * V, tau, V, p, shd);
+  int u = 0, len = 0;
+  int32_t* onodes = a.out_nodes + static_cast<int64_t>(b) * a.Kp1;
+  int32_t* otoks = a.out_tokens + static_cast<int64_t>(b) * a.Kp1;
+  if (tid == 0) onodes[0] = 0;
+  while (true) {
+    int accepted = -1;
+    for (int ci = a.child_start[u]; ci < a.child_start[u + 1]; ++ci) {
+      const int c = a.child_list[ci];
+      const int d = a.depth[c];
+      const int x = tk[c];
+      const float* h = hb + static_cast<int64_t>(d - 1) * V;
+      const double mq = s_mq[d], zq = s_zq[d];
+      const double qx = exp(static_cast<double>(h[x]) / tau - mq) / zq;
+      const double px = p[x];
+      const double alpha = (qx == 0.0) ? 1.0 : fmin(1.0, px / qx);
+      if (static_cast<double>(a.ua[static_cast<int64_t>(b) * a.T + c]) < alpha) {
+        accepted = c;
+        break;
+      }
+      // residual max(0, p - q_d), renormalised
+      double s = 0.0;
+      for (int v = tid; v < V; v += RT) {
+        const double q = exp(static_cast<double>(h[v]) / tau - mq) / zq;
+        const double r = fmax(0.0, p[v] - q);
+        p[v] = r;
+        s += r;
+      }
+      const double Z = block_sum(s, shd);
+      if (Z > 0.0)
+        for (int v = tid; v < V; v += RT) p[v] = p[v] / Z;
+      __syncthreads();
+    }
+    if (accepted < 0) break;
+    if (tid == 0) {
+      otoks[len] = tk[accepted];
+      onodes[len + 1] = accepted;
+    }
+    ++len;
+    u = accepted;
+    softmax_into(a.base + (static_cast<int64_t>(b) * a.T + u) * V, tau, V, p, shd);
+  }
+
+  // inverse CDF with u_sample[b][u]: chunked prefix sums in thread order
+  const int C = (V + RT - 1) / RT;
+  const int v0 = tid * C;
+  const int v1 = min(V, v0 + C);
+  double local = 0.0;
+  for (int v = v0; v < v1; ++v) local += p[v];
+  // exclusive scan of the per-thread sums (wave scan, then wave totals)
+  const int lane = tid & 63, wave = tid >> 6;
+  double incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  __shared__ double s_wsum[RW];
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  double wave_off = 0.0, total = 0.0;
+  for (int w = 0; w < RW; ++w) {
+    if (w < wave) wave_off += s_wsum[w];
+    total += s_wsum[w];
+  }
+  const double thr = static_cast<double>(a.us[static_cast<int64_t>(b) * a.T + u]) * total;
+  double run = wave_off + incl - local;
+  int hit = 0x7fffffff, lastpos = -1;
+  for (int v = v0; v < v1; ++v) {
+    run += p[v];
+    if (run > thr) {
+      hit = v;
+      break;
+    }
+  }
+  for (int v = v0; v < v1; ++v)
+    if (p[v] > 0.0) lastpos = v;
+  hit = block_min_int(hit, shi);
+  lastpos = block_max_int(lastpos, shi);
+  if (tid == 0) {
+    const int y = (hit != 0x7fffffff) ? hit : lastpos;
+    otoks[len] = y;
+    a.acc_len[b] = len;
+    for (int j = len + 1; j < a.Kp1; ++j) {
+      otoks[j] = -1;
+      onodes[j] = -1;
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" size_t medusa_accept_workspace_size(int B, int V, const medusa_tree_t* tree,
+                                               float temperature) {
+  if (B < 1 || V < 1 || !tree) return 0;
+  if (temperature == 0.f) return 0;
+  return round_up(static_cast<size_t>(B) * V * sizeof(double), 256);
+}
+
+extern "C" int medusa_accept_paths(const float* base_logits, const float* head_logits,
+                                   const int32_t* tree_tokens, const medusa_tree_t* tree,
+                                   const float* u_accept, const float* u_sample, float temperature,
+                                   int B, int V, int32_t* accept_len, int32_t* out_tokens,
+                                   int32_t* out_nodes, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  clear_error();
+  int rc = check_tree(tree);
+  if (rc) return rc;
+  MEDUSA_CHECK_ARG(base_logits && tree_tokens && accept_len && out_tokens && out_nodes,
+                   "base_logits, tree_tokens and the outputs must be non-NULL");
+  MEDUSA_CHECK_ARG(B >= 1 && V >= 1, "B=%d and V=%d must be >= 1", B, V);
+  MEDUSA_CHECK_ARG(temperature >= 0.f && temperature < 1e30f,
+                   "temperature=%g must be >= 0 and finite", static_cast<double>(temperature));
+  AcceptArgs a{};
+  a.base = base_logits;
+  a.head = head_logits;
+  a.toks = tree_tokens;
+  a.ua = u_accept;
+  a.us = u_sample;
+  a.child_start = tree->d_child_start;
+  a.child_list = tree->d_child_list;
+  a.depth = tree->d_depth;
+  a.T = tree->T;
+  a.V = V;
+  a.K = tree->K;
+  a.Kp1 = tree->K + 1;
+  a.max_depth = tree->max_depth;
+  a.tau = temperature;
+  a.acc_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.out_nodes = out_nodes;
+  if (temperature == 0.f) {
+    hipLaunchKernelGGL(accept_greedy_kernel, dim3(B), dim3(GT), 0, stream, a);
+    return check_launch("greedy acceptance");
+  }
+  MEDUSA_CHECK_ARG(head_logits && u_accept && u_sample,
+                   "rejection sampling needs head_logits, u_accept and u_sample");
+  const size_t need = medusa_accept_workspace_size(B, V, tree, temperature);
+  if (!ws || ws_bytes < need || !aligned256(ws)) {
+    set_error("acceptance workspace: need %zu bytes, 256-byte aligned (got %zu at %p)", need,
+              ws_bytes, ws);
+    return MEDUSA_EWORKSPACE;
+  }
+  a.pbuf = static_cast<double*>(ws);
+  hipLaunchKernelGGL(accept_reject_kernel, dim3(B), dim3(RT), 0, stream, a);
+  return check_launch("rejection-sampling acceptance");
+}

@@ -1,0 +1,95 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <vector>
+
+#include "medusa.h"
+
+namespace medusa {
+
+// ---- errors --------------------------------------------------------------
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+#define MEDUSA_CHECK_ARG(cond, ...)          \
+  do {                                       \
+    if (!(cond)) {                           \
+      ::medusa::set_error(__VA_ARGS__);      \
+      return MEDUSA_EINVAL;                  \
+    }                                        \
+  } while (0)
+
+#define MEDUSA_HIP_TRY(expr)                                                    \
+  do {                                                                          \
+    hipError_t e_ = (expr);                                                     \
+    if (e_ != hipSuccess) {                                                     \
+      ::medusa::set_error("%s failed: %s", #expr, hipGetErrorString(e_));       \
+      return MEDUSA_EHIP;                                                       \
+    }                                                                           \
+  } while (0)
+
+// after a kernel launch
+int check_launch(const char* what);
+
+// current device id, or -1 with the error set
+int current_device();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace medusa
+
+// ---- the static tree -----------------------------------------------------
+// Device arrays live in one allocation; all are int32 except the mask.
+struct medusa_tree {
+  int T = 0, K = 0, W = 0, max_depth = 0, kmax = 0;
+  int device = -1;
+  std::vector<int32_t> parent, rank, depth, kpd;
+  std::vector<int32_t> child_start;  // [T+1] CSR offsets into child_list
+  std::vector<int32_t> child_list;   // [T-1] children of each node, rank order
+  std::vector<uint64_t> mask;        // [T][W]
+  void* blob = nullptr;
+  const uint64_t* d_mask = nullptr;
+  const int32_t* d_parent = nullptr;
+  const int32_t* d_rank = nullptr;
+  const int32_t* d_depth = nullptr;
+  const int32_t* d_child_start = nullptr;
+  const int32_t* d_child_list = nullptr;
+  const int32_t* d_kpd = nullptr;
+};
+
+namespace medusa {
+// Checks that the tree exists and belongs to the current device.
+int check_tree(const medusa_tree_t* tree);
+}  // namespace medusa
+
+// ---- device helpers ------------------------------------------------------
+namespace medusa {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+}  // namespace dev
+}  // namespace medusa
