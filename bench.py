@@ -5,9 +5,10 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 medusa_heads -> medusa_tree_candidates -> medusa_tree_attention for every
 layer (each layer on its own Q/K/V buffers) -> medusa_accept_paths.  All
 inputs are resident in HBM before timing starts.  The step is captured once
-as a HIP graph and replayed (the host never sits in the timed loop); a second,
-eager pass records HIP events around every stage on the launch stream for the
-per-stage and per-kernel figures.
+as a HIP graph and replayed (the host never sits in the timed loop).  For the
+per-stage and per-kernel figures every stage is captured as a graph of its
+own and replayed between HIP events on the launch stream; the attention
+stage's graph holds all layers, so its time / L is one layer's launch.
 
 Prints one JSON line (see the keys at the end of main()).
 """
@@ -36,7 +37,7 @@ def parse():
     p.add_argument("--workload", default="vicuna7b-shaped")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-layers", type=int, default=4,
+    p.add_argument("--cpu-layers", type=int, default=32,
                    help="attention layers the CPU oracle runs (scaled to all layers)")
     return p.parse_args()
 
@@ -90,8 +91,8 @@ def build_step(w, dev):
                       torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev))
                 for tau in w.temperature}
 
-    def ws(n):
-        return torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    def ws(n):  # zero-filled: some workspaces hold arrival counters
+        return torch.zeros(max(n, 256), dtype=torch.uint8, device=dev)
 
     ws_heads = ws(api.heads_workspace_size(w.B, w.H, w.K, torch.bfloat16))
     ws_attn = ws(api.tree_attention_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.ctx, tree, torch.bfloat16))
@@ -122,6 +123,39 @@ def build_step(w, dev):
     return step, (stage_heads, stage_candidates, stage_attention, stage_accept), keep
 
 
+def _capture(fn):
+    """Capture fn's launches (on torch's current stream) as one HIP graph."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _time_replays(run, reps, warmup):
+    """Mean ms per call of run() between two events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def time_gpu(w, args):
     import torch
 
@@ -129,22 +163,9 @@ def time_gpu(w, args):
     torch.cuda.set_device(dev)
     step, stages, keep = build_step(w, dev)
     torch.cuda.synchronize()
+    stage_heads, stage_candidates, stage_attention, stage_accept = stages
 
-    run = step
-    if not args.eager:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for _ in range(2):
-                step()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        torch.cuda.synchronize()
-        run = g.replay
-
+    run = step if args.eager else _capture(step).replay
     log(f"warmup {args.warmup}, timing {args.steps} steps ({'eager' if args.eager else 'graph'})")
     for _ in range(args.warmup):
         run()
@@ -160,45 +181,24 @@ def time_gpu(w, args):
     wall_s = time.perf_counter() - t_wall
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # instrumented eager pass: events on the launch stream around every stage
-    stage_heads, stage_candidates, stage_attention, stage_accept = stages
-    names = ["heads", "candidates", "attention", "accept"]
-    acc = {n: 0.0 for n in names}
-    attn_calls = 0
-    reps = max(3, min(args.steps, 20))
-    for _ in range(reps):
-        ev = []
-
-        def mark():
-            e = torch.cuda.Event(enable_timing=True)
-            e.record()
-            ev.append(e)
-
-        mark(); stage_heads(); mark(); stage_candidates(); mark()
-        attn_marks = []
+    # per-stage figures: each stage captured as its own graph and replayed
+    # between events on the launch stream (no host time inside)
+    def all_layers():
         for l in range(w.L):
             stage_attention(l)
-            mark()
-            attn_marks.append(len(ev) - 1)
-        stage_accept(); mark()
-        torch.cuda.synchronize()
-        acc["heads"] += ev[0].elapsed_time(ev[1])
-        acc["candidates"] += ev[1].elapsed_time(ev[2])
-        prev = 2
-        for i in attn_marks:
-            acc["attention"] += ev[prev].elapsed_time(ev[i])
-            prev = i
-            attn_calls += 1
-        acc["accept"] += ev[prev].elapsed_time(ev[-1])
-    stages_us = {n: 1000.0 * acc[n] / reps for n in names}
-    attn_call_us = 1000.0 * acc["attention"] / attn_calls
+
+    graphs = {"heads": _capture(stage_heads), "candidates": _capture(stage_candidates),
+              "attention": _capture(all_layers), "accept": _capture(stage_accept)}
+    reps = max(5, args.steps)
+    stages_us = {n: 1000.0 * _time_replays(g.replay, reps, 3) for n, g in graphs.items()}
+    attn_call_us = stages_us["attention"] / w.L
     return ms_per_step, wall_s, stages_us, attn_call_us
 
 
-def cpu_baseline(w, n_layers):
-    """The oracle as it stands (NumPy, fp64) on the host cores, on one step of
-    the same workload with attention run for n_layers layers and scaled to all
-    L layers."""
+def cpu_baseline(w, n_layers, min_seconds=10.0, max_steps=5):
+    """The oracle as it stands (NumPy, fp64) on the host cores: whole steps of
+    the same workload (attention on n_layers of the L layers, scaled to all
+    L), repeated until about min_seconds of CPU work have been timed."""
     import numpy as np
     import torch
     from medusa_tree_verification_amd import synth
@@ -213,44 +213,51 @@ def cpu_baseline(w, n_layers):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
+    n_layers = min(n_layers, w.L)
     parent, rank = synth.cost_ordered_tree(w.topk, w.T)
-    hidden, w1, wlm = synth.head_inputs(w, "cpu")
     f64 = lambda t: t.to(torch.float64).numpy()
-    t0 = time.perf_counter()
-    logits = oheads.medusa_heads(f64(hidden), f64(w1), f64(wlm), round_r=w.dtype == "bf16")
-    t_heads = time.perf_counter() - t0
+    hidden, w1, wlm = synth.head_inputs(w, "cpu")
+    h64, w1_64, wlm64 = f64(hidden), f64(w1), f64(wlm)
     del w1, wlm
-    t0 = time.perf_counter()
-    tk = otopk.head_topk(logits, w.topk)
-    toks = otree.tree_tokens(tk, synth.roots(w, "cpu").numpy(), parent, rank)
-    vis = otree.visible_bruteforce(parent)
-    t_cand = time.perf_counter() - t0
-    t_attn = 0.0
+    layers = []
     for l in range(n_layers):
         q, k, v, ctx = synth.attention_inputs(w, l, "cpu")
-        qd, kd, vd = f64(q), f64(k), f64(v)
+        layers.append((f64(q), f64(k), f64(v), ctx.numpy()))
+    base = synth.normal((w.B, w.T, w.V), w.base_logit_std, synth.seed_for(w.cfg_id, synth.T_BASE)).numpy()
+    ua = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_UACC)).numpy()
+    us = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_USMP)).numpy()
+    roots = synth.roots(w, "cpu").numpy()
+    tot = {"heads": 0.0, "candidates": 0.0, "attention": 0.0, "accept": 0.0}
+    steps = 0
+    while steps < max_steps and (steps == 0 or sum(tot.values()) < min_seconds):
         t0 = time.perf_counter()
-        oattn.tree_attention(qd, kd, vd, ctx.numpy(), vis)
-        t_attn += time.perf_counter() - t0
-    t_attn *= w.L / n_layers
-    base = synth.normal((w.B, w.T, w.V), w.base_logit_std, synth.seed_for(w.cfg_id, synth.T_BASE))
-    ua = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_UACC))
-    us = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_USMP))
-    t0 = time.perf_counter()
-    for tau in w.temperature:
-        oaccept.accept_paths(base.numpy(), logits, toks, parent, rank, ua.numpy(), us.numpy(),
-                             tau, w.K)
-    t_acc = time.perf_counter() - t0
-    total = t_heads + t_cand + t_attn + t_acc
+        logits = oheads.medusa_heads(h64, w1_64, wlm64, round_r=w.dtype == "bf16")
+        t1 = time.perf_counter()
+        tk = otopk.head_topk(logits, w.topk)
+        toks = otree.tree_tokens(tk, roots, parent, rank)
+        vis = otree.visible_bruteforce(parent)
+        t2 = time.perf_counter()
+        for (qd, kd, vd, cl) in layers:
+            oattn.tree_attention(qd, kd, vd, cl, vis)
+        t3 = time.perf_counter()
+        for tau in w.temperature:
+            oaccept.accept_paths(base, logits, toks, parent, rank, ua, us, tau, w.K)
+        t4 = time.perf_counter()
+        tot["heads"] += t1 - t0
+        tot["candidates"] += t2 - t1
+        tot["attention"] += (t3 - t2) * w.L / n_layers
+        tot["accept"] += t4 - t3
+        steps += 1
+    per_step = sum(tot.values()) / steps
     return {
-        "value": 1.0 / total,
+        "value": 1.0 / per_step,
         "unit": "verify steps/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"one {w.name} step: heads, top-k/tree, acceptance in full; tree attention "
-                   f"on {n_layers} of {w.L} layers, scaled x{w.L / n_layers:g} (fp64 NumPy)"),
-        "stage_s": {"heads": round(t_heads, 3), "candidates": round(t_cand, 3),
-                    "attention": round(t_attn, 3), "accept": round(t_acc, 3)},
+        "sample": (f"{steps} {w.name} step(s): heads, top-k/tree and acceptance in full, tree "
+                   f"attention on {n_layers} of {w.L} layers scaled x{w.L / n_layers:g} "
+                   f"(fp64 NumPy); {sum(tot.values()):.1f} s of CPU work timed"),
+        "stage_s": {k: round(v / steps, 3) for k, v in tot.items()},
     }
 
 
@@ -274,7 +281,7 @@ def main():
     attn_total = stages_us["attention"]
     dominant_attention = attn_total >= stages_us["heads"]
     if dominant_attention:
-        roof = {"kernel": "tree_attn_bf16 (+ split merge), one layer", "bound": "hbm",
+        roof = {"kernel": "tree_attn_bf16, one layer", "bound": "hbm",
                 "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                 "bytes_per_launch": a_bytes, "us_per_launch": round(attn_us, 2)}

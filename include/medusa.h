@@ -31,7 +31,10 @@
  *     same thread).  No exception crosses the ABI.
  *   - Scratch memory is passed in by the caller (ws, ws_bytes, sized by the
  *     matching *_workspace_size call, 256-byte aligned).  No call allocates
- *     device memory except medusa_tree_create.
+ *     device memory except medusa_tree_create.  Workspaces of
+ *     medusa_tree_attention and of greedy medusa_accept_paths hold arrival
+ *     counters: zero-fill them once before their first use; every call
+ *     leaves them zero-filled again.
  *   - Floating-point inputs must be finite.  Non-finite inputs give
  *     unspecified outputs, but every kernel still terminates and every index
  *     written stays in its documented range (or -1).
@@ -189,7 +192,8 @@ int medusa_tree_candidates(const float* head_logits, const int32_t* root,
  * scores, sums and accumulators; bf16 operands use MFMA.
  * Constraints: Hq % Hkv == 0; D = 128 (bf16) or D <= 128, D % 4 == 0 (f32);
  * T = the tree's T; S_cap >= ctx_max + T.  Pointers 16-byte aligned.
- * Workspace: split partials (see medusa_tree_attention_workspace_size).
+ * Workspace: split partials and one arrival counter per (b, K/V head, query
+ * chunk); zero-filled before first use (0 bytes when no split is needed).
  * ------------------------------------------------------------------------ */
 size_t medusa_tree_attention_workspace_size(int B, int Hq, int Hkv, int D, int ctx_max,
                                             const medusa_tree_t* tree, medusa_dtype_t dt);
@@ -227,7 +231,9 @@ int medusa_tree_attention(const void* q, const void* k_cache, const void* v_cach
  *   accept_len  [B] int32 (output) number of accepted tree nodes, 0..max depth
  *   out_tokens  [B][K+1] int32 (output) accept_len + 1 emitted tokens, -1 after
  *   out_nodes   [B][K+1] int32 (output) root (0) then the accepted nodes, -1 after
- * Workspace: rejection sampling keeps one fp64 distribution per sequence.
+ * Workspace: greedy keeps each node's argmax and one arrival counter per
+ * sequence (zero-filled before first use); rejection sampling keeps one fp64
+ * distribution per sequence.
  * ------------------------------------------------------------------------ */
 size_t medusa_accept_workspace_size(int B, int V, const medusa_tree_t* tree,
                                     float temperature);

@@ -110,10 +110,12 @@ class Tree:
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
-    if nbytes == 0:
-        return ws, 0
+    """A caller's workspace, or a new zero-filled one (the attention and greedy
+    acceptance workspaces hold arrival counters that must start at zero)."""
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if nbytes == 0:
+            return None, 0
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 

@@ -26,6 +26,8 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs (no AGPR copies around the softmax)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]

@@ -15,10 +15,12 @@
 // next), an accepted child becomes the current node, and the walk ends with
 // one token drawn from the current p by inverse CDF.
 //
-// One workgroup per sequence.  The walk is sequential by nature; each step
-// is a block-wide pass over the vocabulary.  Probabilities are fp64 so that
-// the accept/reject decisions and the sampled token agree with an fp64
-// reference except in ties at the 1e-12 level.
+// Greedy: one workgroup per (node, sequence) takes the target's argmax of
+// that node (first maximum), then the last workgroup of the sequence walks
+// the tree.  Rejection sampling: one workgroup per sequence, since the walk is
+// sequential by nature; each step is a block-wide pass over the vocabulary.
+// Probabilities are fp64 so that the accept/reject decisions and the sampled
+// token agree with an fp64 reference except in ties at the 1e-12 level.
 #include "internal.h"
 
 using namespace medusa;
@@ -43,95 +45,116 @@ struct AcceptArgs {
   int32_t* acc_len;
   int32_t* out_tokens;
   int32_t* out_nodes;
-  double* pbuf;        // [B][V]
+  double* pbuf;        // [B][V]       (rejection)
+  int32_t* argmax;     // [B][T]       (greedy)
+  int* counters;       // [B], zero between calls (greedy)
 };
 
 // ---------------------------------------------------------------------------
-// greedy
+// greedy: the target's argmax of every tree node in parallel (one workgroup
+// per node and sequence, the whole row in flight at once), then the last
+// workgroup of a sequence to finish walks the tree over those argmaxes.
 // ---------------------------------------------------------------------------
-constexpr int GT = 256;
+constexpr int GT = 1024;
 
 __global__ __launch_bounds__(GT) void accept_greedy_kernel(AcceptArgs a) {
-  const int b = blockIdx.x;
+  const int n = blockIdx.x;
+  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   __shared__ float s_v[GT / 64];
   __shared__ int s_i[GT / 64];
-  __shared__ int s_next, s_tok;
-  int u = 0, len = 0, t = -1;
-  int32_t* onodes = a.out_nodes + static_cast<int64_t>(b) * a.Kp1;
-  int32_t* otoks = a.out_tokens + static_cast<int64_t>(b) * a.Kp1;
-  for (int iter = 0; iter <= a.max_depth; ++iter) {
-    const float* row = a.base + (static_cast<int64_t>(b) * a.T + u) * a.V;
-    float bv = -INFINITY;
-    int bi = -1;
+  const float* row = a.base + (static_cast<int64_t>(b) * a.T + n) * a.V;
+  float bv = -INFINITY;
+  int bi = -1;
+  if ((a.V & 3) == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0) {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    const int n4 = a.V >> 2;
     int v = tid;
-    for (; v + 7 * GT < a.V; v += 8 * GT) {
-      float buf[8];
+    for (; v + 7 * GT < n4; v += 8 * GT) {
+      float4 buf[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) buf[k] = row[v + k * GT];
+      for (int k = 0; k < 8; ++k) buf[k] = r4[v + k * GT];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (beats(buf[k], v + k * GT, bv, bi)) {
-          bv = buf[k];
-          bi = v + k * GT;
-        }
+      for (int k = 0; k < 8; ++k) {
+        const int i0 = 4 * (v + k * GT);
+        if (beats(buf[k].x, i0, bv, bi)) { bv = buf[k].x; bi = i0; }
+        if (beats(buf[k].y, i0 + 1, bv, bi)) { bv = buf[k].y; bi = i0 + 1; }
+        if (beats(buf[k].z, i0 + 2, bv, bi)) { bv = buf[k].z; bi = i0 + 2; }
+        if (beats(buf[k].w, i0 + 3, bv, bi)) { bv = buf[k].w; bi = i0 + 3; }
+      }
     }
-    for (; v < a.V; v += GT)
+    for (; v < n4; v += GT) {
+      const float4 f = r4[v];
+      const int i0 = 4 * v;
+      if (beats(f.x, i0, bv, bi)) { bv = f.x; bi = i0; }
+      if (beats(f.y, i0 + 1, bv, bi)) { bv = f.y; bi = i0 + 1; }
+      if (beats(f.z, i0 + 2, bv, bi)) { bv = f.z; bi = i0 + 2; }
+      if (beats(f.w, i0 + 3, bv, bi)) { bv = f.w; bi = i0 + 3; }
+    }
+  } else {
+    for (int v = tid; v < a.V; v += GT)
       if (beats(row[v], v, bv, bi)) {
         bv = row[v];
         bi = v;
       }
+  }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off, 64);
-      int oi = __shfl_xor(bi, off, 64);
-      if (beats(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off, 64);
+    const int oi = __shfl_xor(bi, off, 64);
+    if (beats(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    s_v[wave] = bv;
+    s_i[wave] = bi;
+  }
+  __syncthreads();
+  if (tid != 0) return;  // the rest is one thread's work
+  float wv = s_v[0];
+  int wi = s_i[0];
+  for (int w = 1; w < GT / 64; ++w)
+    if (beats(s_v[w], s_i[w], wv, wi)) {
+      wv = s_v[w];
+      wi = s_i[w];
+    }
+  a.argmax[static_cast<int64_t>(b) * a.T + n] = wi;
+  __threadfence();  // the argmax is visible device-wide before the count
+  const int old = atomicAdd(a.counters + b, 1);
+  if (old != a.T - 1) return;
+  __threadfence();  // every node's argmax is visible from here on
+  a.counters[b] = 0;  // ready for the next call
+  const int32_t* am = a.argmax + static_cast<int64_t>(b) * a.T;
+  const int32_t* tk = a.toks + static_cast<int64_t>(b) * a.T;
+  int32_t* onodes = a.out_nodes + static_cast<int64_t>(b) * a.Kp1;
+  int32_t* otoks = a.out_tokens + static_cast<int64_t>(b) * a.Kp1;
+  int u = 0, len = 0;
+  while (true) {
+    onodes[len] = u;
+    const int t = am[u];
+    int nxt = -1;
+    for (int ci = a.child_start[u]; ci < a.child_start[u + 1]; ++ci) {
+      const int c = a.child_list[ci];
+      if (tk[c] == t) {
+        nxt = c;
+        break;
       }
     }
-    if (lane == 0) {
-      s_v[wave] = bv;
-      s_i[wave] = bi;
+    if (nxt < 0 || len >= a.max_depth) {
+      otoks[len] = t;
+      break;
     }
-    __syncthreads();
-    if (tid == 0) {
-      float wv = s_v[0];
-      int wi = s_i[0];
-      for (int w = 1; w < GT / 64; ++w)
-        if (beats(s_v[w], s_i[w], wv, wi)) {
-          wv = s_v[w];
-          wi = s_i[w];
-        }
-      int nxt = -1;
-      for (int ci = a.child_start[u]; ci < a.child_start[u + 1]; ++ci) {
-        const int c = a.child_list[ci];
-        if (a.toks[static_cast<int64_t>(b) * a.T + c] == wi) {
-          nxt = c;
-          break;
-        }
-      }
-      s_tok = wi;
-      s_next = nxt;
-      onodes[len] = u;
-    }
-    __syncthreads();
-    t = s_tok;
-    const int nxt = s_next;
-    __syncthreads();  // s_* are rewritten next iteration
-    if (nxt < 0) break;
-    if (tid == 0) otoks[len] = a.toks[static_cast<int64_t>(b) * a.T + nxt];
+    otoks[len] = tk[nxt];
     ++len;
     u = nxt;
   }
-  if (tid == 0) {
-    otoks[len] = t;
-    a.acc_len[b] = len;
-    for (int j = len + 1; j < a.Kp1; ++j) {
-      otoks[j] = -1;
-      onodes[j] = -1;
-    }
+  a.acc_len[b] = len;
+  for (int j = len + 1; j < a.Kp1; ++j) {
+    otoks[j] = -1;
+    onodes[j] = -1;
   }
 }
 
@@ -328,7 +351,8 @@ __global__ __launch_bounds__(RT) void accept_reject_kernel(AcceptArgs a) {
 extern "C" size_t medusa_accept_workspace_size(int B, int V, const medusa_tree_t* tree,
                                                float temperature) {
   if (B < 1 || V < 1 || !tree) return 0;
-  if (temperature == 0.f) return 0;
+  if (temperature == 0.f)
+    return round_up(static_cast<size_t>(B) * tree->T * 4, 256) + round_up(static_cast<size_t>(B) * 4, 256);
   return round_up(static_cast<size_t>(B) * V * sizeof(double), 256);
 }
 
@@ -364,17 +388,21 @@ extern "C" int medusa_accept_paths(const float* base_logits, const float* head_l
   a.acc_len = accept_len;
   a.out_tokens = out_tokens;
   a.out_nodes = out_nodes;
-  if (temperature == 0.f) {
-    hipLaunchKernelGGL(accept_greedy_kernel, dim3(B), dim3(GT), 0, stream, a);
-    return check_launch("greedy acceptance");
-  }
-  MEDUSA_CHECK_ARG(head_logits && u_accept && u_sample,
-                   "rejection sampling needs head_logits, u_accept and u_sample");
+  if (temperature != 0.f)
+    MEDUSA_CHECK_ARG(head_logits && u_accept && u_sample,
+                     "rejection sampling needs head_logits, u_accept and u_sample");
   const size_t need = medusa_accept_workspace_size(B, V, tree, temperature);
   if (!ws || ws_bytes < need || !aligned256(ws)) {
     set_error("acceptance workspace: need %zu bytes, 256-byte aligned (got %zu at %p)", need,
               ws_bytes, ws);
     return MEDUSA_EWORKSPACE;
+  }
+  if (temperature == 0.f) {
+    a.argmax = static_cast<int32_t*>(ws);
+    a.counters = reinterpret_cast<int*>(static_cast<char*>(ws) +
+                                        round_up(static_cast<size_t>(B) * tree->T * 4, 256));
+    hipLaunchKernelGGL(accept_greedy_kernel, dim3(tree->T, B), dim3(GT), 0, stream, a);
+    return check_launch("greedy acceptance");
   }
   a.pbuf = static_cast<double*>(ws);
   hipLaunchKernelGGL(accept_reject_kernel, dim3(B), dim3(RT), 0, stream, a);

@@ -6,36 +6,41 @@
 // P4 ("추측 디코딩과 긴 컨텍스트"), section 3.3: attention over separate key
 // blocks can be merged exactly by tracking the running max and exp-sum (the
 // online softmax), which is what lets the key range be cut into splits and
-// waves here and merged afterwards.
+// merged afterwards.
 //
 // bf16 design (gfx950, D = 128)
 //   Work item: one workgroup (4 waves) per (sequence b, K/V head, query chunk,
 //   key split).  All T*G query rows of a K/V head (G = Hq/Hkv; row r = node
-//   r/G, query head r%G) are handled by the same workgroup, so every K/V byte
-//   of the split is read from HBM once.  The 4 waves are QG query groups x KS
-//   key sub-splits; a wave owns QTW tiles of 16 query rows and every KS-th
-//   32-key block of the split.
-//   Scores: S^T = K Q^T on v_mfma_f32_16x16x32_bf16, K as the A operand read
-//   straight from HBM (lane l: key l%16, 64 contiguous bytes of d), Q as B
-//   kept in registers for the whole kernel.  The d order is permuted the same
-//   way in both operands.  Result layout: lane l holds query l%16 and 4
-//   consecutive keys, so every lane's softmax state (max, sum, rescale) is
-//   its own query's.
-//   Values: O^T += V^T P^T.  The MFMA wants 8 consecutive keys of one d per
-//   lane, V is stored [key][d], so each wave transposes its V block through a
-//   private LDS tile: rows = d, 4-key granules of 8 bytes, rows padded to 72
-//   bytes and granules XOR-swizzled by (d/16)%8, which keeps both the
-//   transposing 8-byte writes and the 8-byte operand reads free of bank
-//   conflicts.  P^T comes straight from the score registers (converted to
-//   bf16) because the key order of the MFMA k-slots is chosen to match them.
+//   r/G, query head r%G) go through the same pass over its keys, so every K/V
+//   byte of the split is read from HBM once.  The query tiles (16 rows) of
+//   the chunk are dealt round-robin to the 4 waves; every wave consumes every
+//   32-key block.
+//   Staging: the workgroup streams its key range in 32-key blocks (16 KB of
+//   K and V).  Each thread loads 64 bytes of every block into registers,
+//   three blocks ahead of use, then writes them to a ring of LDS slots: half
+//   the threads store K rows with their 16-byte chunks XOR-swizzled by key
+//   (conflict-free MFMA operand reads), the other half hold 4 keys x 8 d of V
+//   and store them transposed (rows = d, 4-key granules of 8 bytes, rows
+//   padded to 72 bytes, granules swizzled by (d/16)%8) -- the layout the
+//   P.V product needs.  One barrier per block; a slot is rewritten only
+//   after every wave has passed the barrier that follows its last use.
+//   Scores: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows as the A
+//   operand, Q rows, staged once in LDS, as B; the d order is permuted the
+//   same way in both).  Lane l then holds query l%16 and 4 keys, so every
+//   lane's softmax state (max, sum, rescale) is its own query's.
+//   Values: O^T += V^T P^T; P^T comes straight from the score registers
+//   (packed to bf16) because the key order of the MFMA k-slots is chosen to
+//   match them.
 //   Mask: context keys are always visible; tree key j is visible to node i
-//   iff bit j of node i's ancestor bitmask is set (rows staged in LDS).  Only
+//   iff bit j of node i's ancestor bitmask is set (rows staged in LDS); only
 //   blocks that reach past the context evaluate it.
 //   exp2 with log2(e) folded into the scale; fp32 scores, sums and outputs.
-//   Partials of a split (unnormalised O, max, sum) go to the workspace and a
-//   second kernel merges the splits in a fixed order (deterministic).
-//   Workgroups are numbered so that all splits of one (b, K/V head) land on
-//   the same XCD (dispatch assigns workgroup i to XCD i % 8).
+//   Splits: each workgroup writes its partial (unnormalised O, max, sum); a
+//   second kernel merges the splits of every row in split order (fixed
+//   order: deterministic).  Workgroups are numbered so that all splits of one
+//   (b, K/V head) land on the same XCD (dispatch assigns workgroup i to XCD
+//   i % 8), which keeps their partials in one L2.
+#include <cmath>
 #include <cstdlib>
 
 #include "internal.h"
@@ -46,10 +51,19 @@ using namespace medusa::dev;
 namespace {
 
 constexpr int D = 128;
-constexpr int KB = 32;                 // keys per block
-constexpr int VROWB = 72;              // bytes per V^T row in LDS (64 + 8 pad)
-constexpr int VT_BYTES = D * VROWB;    // one wave's V^T tile
+constexpr int KB = 64;                  // keys per staged block
+constexpr int HALF = 32;                // keys per compute half (one P.V MFMA k-step)
+constexpr int VROWB = 72;               // bytes per V^T row (64 + 8 pad)
+constexpr int VT_BYTES = D * VROWB;     // one 32-key V^T tile: 9216
+constexpr int KROWB = D * 2;            // 256 bytes per K row
+constexpr int K_BYTES = KB * KROWB;     // 16384
+constexpr int SLOT_BYTES = K_BYTES + 2 * VT_BYTES;
+constexpr int QROW_CHUNKS = D / 8;      // 16-byte chunks per Q / K row
+constexpr int PREFETCH = 2;             // blocks in flight per workgroup (= LDS slots)
+constexpr int RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr float LOG2E = 1.4426950408889634f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
   const uint16_t* q;
@@ -64,14 +78,8 @@ struct AttnArgs {
   uint16_t* out;
   float* part_o;   // [NS][B*Hkv][QRpad][D]
   float* part_ml;  // [NS][B*Hkv][QRpad][2]
-  int mask_bytes;  // LDS bytes reserved for the mask rows
+  int lds_mask, lds_q, lds_ring;  // dynamic LDS layout (byte offsets)
 };
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 __device__ __forceinline__ float wave_max_16_32(float x) {
   x = fmaxf(x, __shfl_xor(x, 16, 64));
@@ -83,61 +91,130 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-template <int QTW>
-struct KVRegs {
-  uint4 k[2][4];  // [16-key subtile][d step]
-  uint4 v[2][4];  // [quad half][key in quad]
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+struct Stage {
+  uint4 k[4];  // 64 bytes of one K row
+  uint4 v[4];  // 4 keys x 8 d of V
 };
 
-template <int QTW, int QG, int KS>
+template <int QTW>
 __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int id = blockIdx.x;
   const int task = (id & 7) * a.per_xcd + (id >> 3);
   if (task >= a.tasks) return;  // whole workgroup leaves before any barrier
   const int split = task % a.NS;
-  const int rest = task / a.NS;
+  const int rest = task / a.NS;  // = bh * QC + qc
   const int qc = rest % a.QC;
   const int bh = rest / a.QC;
   const int b = bh / a.Hkv;
   const int kvh = bh % a.Hkv;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int qg = wave / KS;
-  const int ks = wave % KS;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int grp = lane >> 4;
-
-  uint64_t* smask = reinterpret_cast<uint64_t*>(smem);
-  float* sml = reinterpret_cast<float*>(smem + a.mask_bytes);           // [4][QTW*16][2]
-  char* sbig = smem + a.mask_bytes + 4 * QTW * 16 * 2 * 4;               // V^T tiles / merge
-  for (int i = threadIdx.x; i < a.T * a.W; i += 256) smask[i] = a.mask[i];
-  __syncthreads();
 
   int ctx = a.ctx[b];
   ctx = ctx < 0 ? 0 : (ctx > a.S_cap - a.T ? a.S_cap - a.T : ctx);
   const int S = ctx + a.T;
   const int k_begin = split * a.chunk;
   const int k_end = (split == a.NS - 1) ? S : min(S, k_begin + a.chunk);
+  const int nblk = k_end > k_begin ? (k_end - k_begin + KB - 1) / KB : 0;
 
-  // ---- Q fragments (B operand of S^T = K Q^T) ----
-  const int row_base = (qc * QG + qg) * QTW * 16;
-  uint4 qf[QTW][4];
+  // K/V of this (b, head) as buffer resources limited to the split's end:
+  // reads of keys >= k_end return zeros (never the unused cache slots)
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.k + static_cast<int64_t>(bh) * a.S_cap * D), 0, k_end * KROWB, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.v + static_cast<int64_t>(bh) * a.S_cap * D), 0, k_end * KROWB, RSRC_WORD3);
+
+  // staging roles (every thread): K row tid/4, 16-byte chunks 4*(tid%4)..+3;
+  // V keys 4*(tid/16)..+3 at d-octet tid%16
+  const int k_row = tid >> 2, k_ch = (tid & 3) * 4;
+  const int v_quad = tid >> 4, v_oct = tid & 15;
+  auto gload = [&](Stage& st, int blk) __attribute__((always_inline)) {
+    const int kb = k_begin + blk * KB;
+    const int ko = (kb + k_row) * KROWB + k_ch * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.k[i] = bload16(rk, ko + 16 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.v[i] = bload16(rv, (kb + 4 * v_quad + i) * KROWB + v_oct * 16);
+  };
+  auto lds_put = [&](const Stage& st, char* slot) __attribute__((always_inline)) {
+    uint4* row = reinterpret_cast<uint4*>(slot + k_row * KROWB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) row[(k_ch + i) ^ (k_row & 15)] = st.k[i];
+    // V: 4 keys x 8 d -> 8 granules (4 keys of one d) of this half's V^T tile
+    char* vt = slot + K_BYTES + (v_quad >> 3) * VT_BYTES;
+    const int qd = v_quad & 7;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * v_oct + e;
+      const uint32_t a0 = reinterpret_cast<const uint32_t*>(&st.v[0])[e >> 1];
+      const uint32_t a1 = reinterpret_cast<const uint32_t*>(&st.v[1])[e >> 1];
+      const uint32_t a2 = reinterpret_cast<const uint32_t*>(&st.v[2])[e >> 1];
+      const uint32_t a3 = reinterpret_cast<const uint32_t*>(&st.v[3])[e >> 1];
+      uint32_t w0, w1;
+      if ((e & 1) == 0) {
+        w0 = (a0 & 0xffffu) | (a1 << 16);
+        w1 = (a2 & 0xffffu) | (a3 << 16);
+      } else {
+        w0 = (a0 >> 16) | (a1 & 0xffff0000u);
+        w1 = (a2 >> 16) | (a3 & 0xffff0000u);
+      }
+      *reinterpret_cast<uint2*>(vt + d * VROWB + ((qd ^ ((d >> 4) & 7)) * 8)) = make_uint2(w0, w1);
+    }
+  };
+
+  // ---- prologue: Q rows and mask rows first, then the first blocks ----
+  constexpr int ROWS_WG = 4 * QTW * 16;
+  constexpr int Q_PER_THREAD = ROWS_WG * QROW_CHUNKS / 256;  // 4 * QTW
+  const int row0 = qc * ROWS_WG;
+  uint4 qv[Q_PER_THREAD];
+#pragma unroll
+  for (int u = 0; u < Q_PER_THREAD; ++u) {
+    const int idx = tid + 256 * u;
+    const int rr = idx / QROW_CHUNKS, ch = idx % QROW_CHUNKS;
+    const int r = min(row0 + rr, a.QR - 1);
+    const int node = r / a.G, gq = r % a.G;
+    qv[u] = ldg16(a.q + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + ch * 8);
+  }
+  const int nmask = a.T * a.W;
+  uint64_t mv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) mv[u] = (tid + 256 * u < nmask) ? a.mask[tid + 256 * u] : 0ull;
+  Stage s0, s1;
+  if (nblk > 0) gload(s0, 0);
+  if (nblk > 1) gload(s1, 1);
+  uint4* sq = reinterpret_cast<uint4*>(smem + a.lds_q);
+#pragma unroll
+  for (int u = 0; u < Q_PER_THREAD; ++u) {
+    const int idx = tid + 256 * u;
+    const int rr = idx / QROW_CHUNKS, ch = idx % QROW_CHUNKS;
+    sq[rr * QROW_CHUNKS + (ch ^ (rr & 15))] = (row0 + rr < a.QR) ? qv[u] : make_uint4(0, 0, 0, 0);
+  }
+  uint64_t* smask = reinterpret_cast<uint64_t*>(smem + a.lds_mask);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (tid + 256 * u < nmask) smask[tid + 256 * u] = mv[u];
+
+  // this wave's query tiles: wave, wave + 4, ...
   int qnode[QTW];
 #pragma unroll
   for (int t = 0; t < QTW; ++t) {
-    const int r = row_base + t * 16 + l16;
-    const bool ok = r < a.QR;
-    const int node = ok ? r / a.G : 0;
-    const int gq = ok ? r % a.G : 0;
-    qnode[t] = node;
-    const uint16_t* qp =
-        a.q + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + grp * 32;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qf[t][s] = ok ? ldg16(qp + 8 * s) : make_uint4(0, 0, 0, 0);
+    const int r = row0 + (wave + 4 * t) * 16 + l16;
+    qnode[t] = r < a.QR ? r / a.G : 0;
   }
-
   f32x4 o[QTW][8];
   float m_run[QTW], l_run[QTW];
 #pragma unroll
@@ -147,92 +224,49 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  char* ring = smem + a.lds_ring;
 
-  const uint16_t* kbase = a.k + static_cast<int64_t>(bh) * a.S_cap * D;
-  const uint16_t* vbase = a.v + static_cast<int64_t>(bh) * a.S_cap * D;
-  char* vt = sbig + wave * VT_BYTES;
-
-  auto load_kv = [&](KVRegs<QTW>& r, int kb) {
+  // one 32-key half of a staged block
+  auto compute_half = [&](const char* slot, int h, int kb) __attribute__((always_inline)) {
+    bf16x8 kf[2][4];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int key = kb + st * 16 + l16;
-      const bool ok = key < k_end;
-      const uint16_t* p = kbase + static_cast<int64_t>(ok ? key : 0) * D + grp * 32;
+      const uint4* row = reinterpret_cast<const uint4*>(slot + (h * HALF + st * 16 + l16) * KROWB);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) r.k[st][s] = ok ? ldg16(p + 8 * s) : make_uint4(0, 0, 0, 0);
+      for (int s = 0; s < 4; ++s) kf[st][s] = as_bf16x8(row[(grp * 4 + s) ^ l16]);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + 4 * (grp + 4 * h) + i;
-        const bool ok = key < k_end;
-        const uint16_t* p = vbase + static_cast<int64_t>(ok ? key : 0) * D + 8 * l16;
-        r.v[h][i] = ok ? ldg16(p) : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  auto compute = [&](const KVRegs<QTW>& r, int kb) {
-    // V block -> transposed, swizzled LDS tile
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = grp + 4 * h;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * l16 + e;
-        uint32_t w0, w1;
-        const uint32_t a0 = reinterpret_cast<const uint32_t*>(&r.v[h][0])[e >> 1];
-        const uint32_t a1 = reinterpret_cast<const uint32_t*>(&r.v[h][1])[e >> 1];
-        const uint32_t a2 = reinterpret_cast<const uint32_t*>(&r.v[h][2])[e >> 1];
-        const uint32_t a3 = reinterpret_cast<const uint32_t*>(&r.v[h][3])[e >> 1];
-        if ((e & 1) == 0) {
-          w0 = (a0 & 0xffffu) | (a1 << 16);
-          w1 = (a2 & 0xffffu) | (a3 << 16);
-        } else {
-          w0 = (a0 >> 16) | (a1 & 0xffff0000u);
-          w1 = (a2 >> 16) | (a3 & 0xffff0000u);
-        }
-        const int gp = q ^ ((d >> 4) & 7);
-        *reinterpret_cast<uint2*>(vt + d * VROWB + gp * 8) = make_uint2(w0, w1);
-      }
-    }
-    // scores S^T = K Q^T for 2 subtiles x QTW query tiles
     f32x4 sc[2][QTW];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int t = 0; t < QTW; ++t) {
+      const uint4* qrow = sq + ((wave + 4 * t) * 16 + l16) * QROW_CHUNKS;
+      f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < QTW; ++t) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[st][s]), as_bf16x8(qf[t][s]),
-                                                        acc, 0, 0, 0);
-        sc[st][t] = acc * a.scale_log2;
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 qf = as_bf16x8(qrow[(grp * 4 + s) ^ l16]);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][s], qf, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][s], qf, acc1, 0, 0, 0);
       }
+      sc[0][t] = acc0 * a.scale_log2;
+      sc[1][t] = acc1 * a.scale_log2;
     }
-    // mask (only blocks reaching past the context or the end of the split)
-    if (kb + KB > ctx || kb + KB > k_end) {
+    if (kb + HALF > ctx || kb + HALF > k_end) {  // the tree region or the split's end
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = kb + st * 16 + 4 * grp + e;
-          const int j = key - ctx;
+          const int jj = key - ctx;
 #pragma unroll
           for (int t = 0; t < QTW; ++t) {
             bool vis = key < k_end;
-            if (vis && j >= 0) {
-              const uint64_t wd = smask[qnode[t] * a.W + (j >> 6)];
-              vis = (wd >> (j & 63)) & 1ull;
-            }
+            if (vis && jj >= 0) vis = (smask[qnode[t] * a.W + (jj >> 6)] >> (jj & 63)) & 1ull;
             if (!vis) sc[st][t][e] = -INFINITY;
           }
         }
       }
     }
-    // online softmax per query (lane-local state; max shared across the 4 lane groups)
-    bf16x8 pb[QTW];
+    uint4 pb[QTW];
 #pragma unroll
     for (int t = 0; t < QTW; ++t) {
       float bm = fmaxf(fmaxf(fmaxf(sc[0][t][0], sc[0][t][1]), fmaxf(sc[0][t][2], sc[0][t][3])),
@@ -242,54 +276,58 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
       const float muse = (mnew == -INFINITY) ? 0.f : mnew;
       const float alpha = __builtin_amdgcn_exp2f(m_run[t] - muse);
       m_run[t] = mnew;
-      float ps = 0.f;
+      float p[8];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sc[st][t][e] - muse);
-          ps += p;
-          pb[t][st * 4 + e] = static_cast<__bf16>(p);
-        }
+        for (int e = 0; e < 4; ++e) p[st * 4 + e] = __builtin_amdgcn_exp2f(sc[st][t][e] - muse);
+      l_run[t] = l_run[t] * alpha + ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      pb[t] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                         pack_bf16(p[6], p[7]));
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // some query's max moved
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
       }
-      l_run[t] = l_run[t] * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
     }
-    wave_lds_sync();
-    // O^T += V^T P^T
+    const char* vt = slot + K_BYTES + h * VT_BYTES;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int d = dt * 16 + l16;
-      const char* rowp = vt + d * VROWB;
+      const char* rowp = vt + (dt * 16 + l16) * VROWB;
       const uint2 lo = *reinterpret_cast<const uint2*>(rowp + ((grp ^ (dt & 7)) * 8));
       const uint2 hi = *reinterpret_cast<const uint2*>(rowp + (((grp + 4) ^ (dt & 7)) * 8));
       const bf16x8 va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
       for (int t = 0; t < QTW; ++t)
-        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[t], o[t][dt], 0, 0, 0);
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(pb[t]), o[t][dt], 0, 0, 0);
     }
-    wave_lds_sync();
   };
 
-  // ---- main loop: register double buffer over this wave's blocks ----
-  const int stride = KS * KB;
-  int kb = k_begin + ks * KB;
-  if (kb < k_end) {
-    KVRegs<QTW> ra, rb;
-    load_kv(ra, kb);
-    while (true) {
-      const int kb1 = kb + stride;
-      if (kb1 < k_end) load_kv(rb, kb1);
-      compute(ra, kb);
-      if (kb1 >= k_end) break;
-      const int kb2 = kb1 + stride;
-      if (kb2 < k_end) load_kv(ra, kb2);
-      compute(rb, kb1);
-      if (kb2 >= k_end) break;
-      kb = kb2;
-    }
+  // Pipeline: block 0 is staged before the loop; step i computes block i from
+  // its slot while staging block i+1 into the other slot and refilling that
+  // register buffer with block i+1+PREFETCH; one barrier per step.  A slot is
+  // rewritten only after the barrier that follows its last reader.
+  if (nblk > 0) {
+    lds_put(s0, ring);
+    if (PREFETCH < nblk) gload(s0, PREFETCH);
   }
+  __syncthreads();
+  auto step = [&](int blk, Stage& next, int si_cur, int si_next) __attribute__((always_inline)) {
+    const char* cur = ring + si_cur * SLOT_BYTES;
+    const int kb = k_begin + blk * KB;
+    compute_half(cur, 0, kb);
+    if (kb + HALF < k_end) compute_half(cur, 1, kb + HALF);
+    if (blk + 1 < nblk) {
+      lds_put(next, ring + si_next * SLOT_BYTES);
+      if (blk + 1 + PREFETCH < nblk) gload(next, blk + 1 + PREFETCH);
+    }
+    __syncthreads();
+  };
+  int blk = 0;
+  for (; blk + 2 <= nblk; blk += 2) {
+    step(blk, s1, 0, 1);
+    step(blk + 1, s0, 1, 0);
+  }
+  if (blk < nblk) step(blk, s1, 0, 1);
 
   // full per-query sums (each lane group holds a quarter of the keys)
 #pragma unroll
@@ -298,61 +336,11 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
     l_run[t] += __shfl_xor(l_run[t], 32, 64);
   }
 
-  // ---- merge the KS key sub-splits of each query group ----
-  if (KS > 1) {
-    if (grp == 0) {
-#pragma unroll
-      for (int t = 0; t < QTW; ++t) {
-        sml[(wave * QTW * 16 + t * 16 + l16) * 2 + 0] = m_run[t];
-        sml[(wave * QTW * 16 + t * 16 + l16) * 2 + 1] = l_run[t];
-      }
-    }
-    __syncthreads();  // also: every wave has finished with its V^T tile
-#pragma unroll
-    for (int t = 0; t < QTW; ++t) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < KS; ++w)
-        M = fmaxf(M, sml[((qg * KS + w) * QTW * 16 + t * 16 + l16) * 2 + 0]);
-      const float muse = (M == -INFINITY) ? 0.f : M;
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < KS; ++w) {
-        const int idx = ((qg * KS + w) * QTW * 16 + t * 16 + l16) * 2;
-        L += sml[idx + 1] * __builtin_amdgcn_exp2f(sml[idx] - muse);
-      }
-      const float f = __builtin_amdgcn_exp2f(m_run[t] - muse);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[t][dt] *= f;
-      m_run[t] = M;
-      l_run[t] = L;
-    }
-    // waves ks >= 1 hand their O to wave ks == 0 of the same query group
-    f32x4* slot = reinterpret_cast<f32x4*>(sbig);
-    const int per_wave = QTW * 8 * 64;  // f32x4 entries
-    if (ks > 0) {
-      f32x4* dst = slot + (qg * (KS - 1) + (ks - 1)) * per_wave;
-#pragma unroll
-      for (int t = 0; t < QTW; ++t)
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) dst[(t * 8 + dt) * 64 + lane] = o[t][dt];
-    }
-    __syncthreads();
-    if (ks > 0) return;  // no barriers follow
-    for (int w = 1; w < KS; ++w) {
-      const f32x4* src = slot + (qg * (KS - 1) + (w - 1)) * per_wave;
-#pragma unroll
-      for (int t = 0; t < QTW; ++t)
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[t][dt] += src[(t * 8 + dt) * 64 + lane];
-    }
-  }
-
-  // ---- write: final output (one split) or the split's partial ----
+  // ---- one split: the output; several: this split's partial ----
   const int BH = a.B * a.Hkv;
 #pragma unroll
   for (int t = 0; t < QTW; ++t) {
-    const int r = row_base + t * 16 + l16;
+    const int r = row0 + (wave + 4 * t) * 16 + l16;
     if (r >= a.QR) continue;
     if (a.NS == 1) {
       const float inv = 1.0f / l_run[t];
@@ -360,27 +348,23 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
       uint16_t* op = a.out + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const int d = dt * 16 + 4 * grp;
-        const uint32_t lo = f32_to_bf16_bits(o[t][dt][0] * inv) | (f32_to_bf16_bits(o[t][dt][1] * inv) << 16);
-        const uint32_t hi = f32_to_bf16_bits(o[t][dt][2] * inv) | (f32_to_bf16_bits(o[t][dt][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + d) = make_uint2(lo, hi);
+        const f32x4 v = o[t][dt] * inv;
+        *reinterpret_cast<uint2*>(op + dt * 16 + 4 * grp) =
+            make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
       }
     } else {
       const int64_t prow = (static_cast<int64_t>(split) * BH + bh) * a.QRpad + r;
       float* po = a.part_o + prow * D;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = o[t][dt];
-      if (grp == 0) {
-        a.part_ml[prow * 2 + 0] = m_run[t];
-        a.part_ml[prow * 2 + 1] = l_run[t];
-      }
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = o[t][dt];
+      if (grp == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_run[t], l_run[t]);
     }
   }
 }
 
-// Merge the NS split partials of every query row, in split order.
-// grid: ceil(BH*QR / 4); block 256 (one wave per row, 2 d-values per lane)
+// Merge the NS split partials of every query row, in split order (NS <= 64).
+// One wave per row, 2 consecutive d per lane; every split's (max, sum) and
+// output values are requested before any arithmetic (one round trip).
 __global__ __launch_bounds__(256) void merge_splits(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int BH = a.B * a.Hkv;
@@ -388,24 +372,42 @@ __global__ __launch_bounds__(256) void merge_splits(AttnArgs a) {
   if (gr >= static_cast<int64_t>(BH) * a.QR) return;
   const int bh = static_cast<int>(gr / a.QR);
   const int r = static_cast<int>(gr % a.QR);
-  float M = -INFINITY;
-  for (int s = 0; s < a.NS; ++s)
-    M = fmaxf(M, a.part_ml[((static_cast<int64_t>(s) * BH + bh) * a.QRpad + r) * 2]);
+  const int64_t stride = static_cast<int64_t>(BH) * a.QRpad;  // rows between splits
+  const int64_t row = static_cast<int64_t>(bh) * a.QRpad + r;
+  const int ns = a.NS;
+  float2 ml = make_float2(-INFINITY, 0.f);
+  if (lane < ns) ml = *reinterpret_cast<const float2*>(a.part_ml + (lane * stride + row) * 2);
+  float2 ov[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    ov[u] = (u < ns) ? *reinterpret_cast<const float2*>(a.part_o + (u * stride + row) * D + 2 * lane)
+                     : make_float2(0.f, 0.f);
+  float M = ml.x;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   const float muse = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < a.NS; ++s) {
-    const int64_t prow = (static_cast<int64_t>(s) * BH + bh) * a.QRpad + r;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[prow * 2] - muse);
-    L += a.part_ml[prow * 2 + 1] * w;
-    const float2 v = *reinterpret_cast<const float2*>(a.part_o + prow * D + 2 * lane);
-    o0 += v.x * w;
-    o1 += v.y * w;
+  const float w = __builtin_amdgcn_exp2f(ml.x - muse);  // lane s: weight of split s
+  float L = ml.y * w;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const float wu = __shfl(w, u, 64);
+    o0 = fmaf(ov[u].x, wu, o0);
+    o1 = fmaf(ov[u].y, wu, o1);
+  }
+  for (int s = 16; s < ns; ++s) {
+    const float2 v = *reinterpret_cast<const float2*>(a.part_o + (s * stride + row) * D + 2 * lane);
+    const float wu = __shfl(w, s, 64);
+    o0 = fmaf(v.x, wu, o0);
+    o1 = fmaf(v.y, wu, o1);
   }
   const float inv = 1.0f / L;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int node = r / a.G, gq = r % a.G;
   uint16_t* op = a.out + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + 2 * lane;
-  *reinterpret_cast<uint32_t*>(op) = f32_to_bf16_bits(o0 * inv) | (f32_to_bf16_bits(o1 * inv) << 16);
+  *reinterpret_cast<uint32_t*>(op) = pack_bf16(o0 * inv, o1 * inv);
 }
 
 // ---- fp32 path: one wave per (b, node, query head), keys in sequence ----
@@ -466,9 +468,9 @@ __global__ __launch_bounds__(256) void tree_attn_f32(AttnF32Args a) {
 
 // ---- launch planning -------------------------------------------------------
 struct Plan {
-  int G, QR, NQT, QTW, QG, KS, QC, QRpad, NS, chunk;
-  size_t ws_bytes;
-  int lds_bytes;
+  int G, QR, NQT, QTW, QC, QRpad, NS, chunk;
+  size_t ws_bytes, off_ml;
+  int lds_bytes, lds_mask, lds_q, lds_ring;
 };
 
 int env_int(const char* name, int dflt) {
@@ -476,79 +478,110 @@ int env_int(const char* name, int dflt) {
   return s ? std::atoi(s) : dflt;
 }
 
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    hipDeviceProp_t prop;
+    cached[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+                      ? prop.multiProcessorCount
+                      : 256;
+  }
+  return cached[dev];
+}
+
+const void* kernel_for(int qtw) {
+  switch (qtw) {
+    case 1: return reinterpret_cast<const void*>(&tree_attn_bf16<1>);
+    case 2: return reinterpret_cast<const void*>(&tree_attn_bf16<2>);
+    case 3: return reinterpret_cast<const void*>(&tree_attn_bf16<3>);
+    default: return reinterpret_cast<const void*>(&tree_attn_bf16<4>);
+  }
+}
+
+// workgroups of this configuration one CU runs at once (1 if unknown)
+int occupancy(int qtw, int lds) {
+  static int cache[5][8] = {{0}};
+  const int bucket = lds / (20 * 1024);
+  if (bucket < 8 && cache[qtw][bucket]) return cache[qtw][bucket];
+  int n = 0;
+  if (lds > 64 * 1024)
+    (void)hipFuncSetAttribute(kernel_for(qtw), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel_for(qtw), 256, lds) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  if (bucket < 8) cache[qtw][bucket] = n;
+  return n;
+}
+
 Plan make_plan(int B, int Hq, int Hkv, int ctx_max, int T, int W) {
   Plan p{};
   p.G = Hq / Hkv;
   p.QR = T * p.G;
   p.NQT = (p.QR + 15) / 16;
-  // A wave keeps at most 3 query tiles (48 rows) of state in registers; more
-  // query tiles go to more waves of the workgroup (QG groups sharing each K/V
-  // block) and then to more workgroups (QC chunks).
-  if (p.NQT <= 3) {
-    p.QTW = p.NQT;
-    p.QG = 1;
-  } else if (p.NQT <= 6) {
-    p.QG = 2;
-    p.QTW = (p.NQT + 1) / 2;
-  } else {
-    p.QG = 4;
-    const int qc = (p.NQT + 11) / 12;
-    p.QTW = (p.NQT + 4 * qc - 1) / (4 * qc);
-  }
-  p.KS = 4 / p.QG;
-  p.QC = (p.NQT + p.QG * p.QTW - 1) / (p.QG * p.QTW);
+  p.QTW = (p.NQT + 3) / 4;
+  if (p.QTW > 4) p.QTW = 4;
+  p.QC = (p.NQT + 4 * p.QTW - 1) / (4 * p.QTW);
   p.QRpad = p.NQT * 16;
+  p.lds_mask = 0;
+  p.lds_q = static_cast<int>(round_up(static_cast<size_t>(T) * W * 8, 16));
+  p.lds_ring = p.lds_q + 4 * p.QTW * 16 * D * 2;
+  p.lds_bytes = p.lds_ring + PREFETCH * SLOT_BYTES;
   const int Smax = ctx_max + T;
   const int base = B * Hkv * p.QC;
   int ns = env_int("MEDUSA_ATTN_SPLITS", 0);
   if (ns <= 0) {
-    ns = (512 + base - 1) / base;          // about two workgroups per CU
-    const int max_ns = (Smax + 2 * p.KS * KB - 1) / (2 * p.KS * KB);  // >= 2 blocks per wave
-    if (ns > max_ns) ns = max_ns;
-    if (ns < 1) ns = 1;
+    // pick the split count minimising rounds x (fixed cost + keys per split),
+    // counting the workgroups all CUs hold at once
+    const int slots = cu_count() * occupancy(p.QTW, p.lds_bytes);
+    const double fixed_keys = 96.0;  // per-workgroup latency, in key-times
+    double best = 1e300;
+    ns = 1;
+    const int max_ns = (Smax + KB - 1) / KB;  // >= one staged block per split
+    for (int n = 1; n <= max_ns && n <= 64; ++n) {
+      const int rounds = (base * n + slots - 1) / slots;
+      const double t = rounds * (fixed_keys + std::ceil(static_cast<double>(Smax) / n));
+      if (t < best * 0.999) {
+        best = t;
+        ns = n;
+      }
+    }
   }
+  if (ns > 64) ns = 64;  // the merge keeps one split per lane
   int chunk = (Smax + ns - 1) / ns;
   chunk = (chunk + KB - 1) / KB * KB;
   p.chunk = chunk;
   p.NS = (Smax + chunk - 1) / chunk;
   if (p.NS < 1) p.NS = 1;
-  p.ws_bytes = p.NS > 1 ? round_up(static_cast<size_t>(p.NS) * B * Hkv * p.QRpad * (D + 2) * 4, 256)
-                        : 0;
-  const int mask_bytes = static_cast<int>(round_up(static_cast<size_t>(T) * W * 8, 16));
-  const int ml_bytes = 4 * p.QTW * 16 * 2 * 4;
-  const int vt = 4 * VT_BYTES;
-  const int merge = p.KS > 1 ? p.QG * (p.KS - 1) * p.QTW * 8 * 64 * 16 : 0;
-  p.lds_bytes = mask_bytes + ml_bytes + (vt > merge ? vt : merge);
+  if (p.NS > 1) {
+    const size_t rows = static_cast<size_t>(p.NS) * B * Hkv * p.QRpad;
+    p.off_ml = round_up(rows * D * 4, 256);
+    p.ws_bytes = p.off_ml + round_up(rows * 2 * 4, 256);
+  }
   return p;
 }
 
-template <int QTW, int QG, int KS>
-void launch_cfg(const AttnArgs& a, int grid, int lds, hipStream_t s) {
-  hipLaunchKernelGGL((tree_attn_bf16<QTW, QG, KS>), dim3(grid), dim3(256), lds, s, a);
-}
-
-bool launch_bf16(const Plan& p, const AttnArgs& a, int grid, hipStream_t s) {
-#define MEDUSA_CASE(QTW_, QG_, KS_)                                                \
-  if (p.QTW == QTW_ && p.QG == QG_ && p.KS == KS_) {                               \
-    static bool attr_set = false;                                                  \
-    if (!attr_set) {                                                               \
-      (void)hipFuncSetAttribute(                                                   \
-          reinterpret_cast<const void*>(&tree_attn_bf16<QTW_, QG_, KS_>),          \
-          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);                 \
-      attr_set = true;                                                             \
-    }                                                                              \
-    launch_cfg<QTW_, QG_, KS_>(a, grid, p.lds_bytes, s);                           \
-    return true;                                                                   \
+template <int QTW>
+int launch_cfg(const AttnArgs& a, int grid, int lds, hipStream_t s) {
+  if (lds > 64 * 1024) {
+    // above 64 KiB the dynamic LDS size must be allowed explicitly
+    static int allowed = 0;
+    if (lds > allowed) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tree_attn_bf16<QTW>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        set_error("cannot allow %d bytes of dynamic LDS for tree attention: %s", lds,
+                  hipGetErrorString(e));
+        return MEDUSA_EUNSUPPORTED;
+      }
+      allowed = lds;
+    }
   }
-  MEDUSA_CASE(1, 1, 4)
-  MEDUSA_CASE(2, 1, 4)
-  MEDUSA_CASE(3, 1, 4)
-  MEDUSA_CASE(2, 2, 2)
-  MEDUSA_CASE(3, 2, 2)
-  MEDUSA_CASE(2, 4, 1)
-  MEDUSA_CASE(3, 4, 1)
-#undef MEDUSA_CASE
-  return false;
+  hipLaunchKernelGGL((tree_attn_bf16<QTW>), dim3(grid), dim3(256), lds, s, a);
+  return check_launch("tree attention (bf16)");
 }
 
 }  // namespace
@@ -641,16 +674,21 @@ extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const v
   a.per_xcd = (a.tasks + 7) / 8;
   a.scale_log2 = scale * LOG2E;
   a.out = static_cast<uint16_t*>(out);
-  a.part_o = p.NS > 1 ? static_cast<float*>(ws) : nullptr;
-  a.part_ml = p.NS > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                                  static_cast<size_t>(p.NS) * B * Hkv * p.QRpad * D * 4)
-                       : nullptr;
-  a.mask_bytes = static_cast<int>(round_up(static_cast<size_t>(tree->T) * tree->W * 8, 16));
-  if (!launch_bf16(p, a, 8 * a.per_xcd, stream)) {
-    set_error("no tree attention kernel for QTW=%d QG=%d KS=%d", p.QTW, p.QG, p.KS);
-    return MEDUSA_EUNSUPPORTED;
+  if (p.NS > 1) {
+    char* w = static_cast<char*>(ws);
+    a.part_o = reinterpret_cast<float*>(w);
+    a.part_ml = reinterpret_cast<float*>(w + p.off_ml);
   }
-  rc = check_launch("tree attention (bf16)");
+  a.lds_mask = p.lds_mask;
+  a.lds_q = p.lds_q;
+  a.lds_ring = p.lds_ring;
+  const int grid = 8 * a.per_xcd;
+  switch (p.QTW) {
+    case 1: rc = launch_cfg<1>(a, grid, p.lds_bytes, stream); break;
+    case 2: rc = launch_cfg<2>(a, grid, p.lds_bytes, stream); break;
+    case 3: rc = launch_cfg<3>(a, grid, p.lds_bytes, stream); break;
+    default: rc = launch_cfg<4>(a, grid, p.lds_bytes, stream); break;
+  }
   if (rc || p.NS == 1) return rc;
   const int64_t rows = static_cast<int64_t>(B) * Hkv * p.QR;
   hipLaunchKernelGGL(merge_splits, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream, a);

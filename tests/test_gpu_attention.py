@@ -147,3 +147,22 @@ def test_attention_argument_errors():
     with pytest.raises(api.MedusaError) as e:                 # bf16 D = 64
         api.tree_attention(q64, kv64, kv64, ctx, 64, t)
     assert e.value.code == api.EUNSUPPORTED
+
+
+def test_attention_workspace_reused_across_calls():
+    """Consecutive calls sharing one workspace (as the layers of a step do):
+    the arrival counters must come back to zero after every call."""
+    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=2, Hq=8, Hkv=4, ctx=1500, cfg_id=260)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    t = api.Tree(parent, rank, w.topk)
+    nb = api.tree_attention_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.ctx, t, torch.bfloat16)
+    assert nb > 0
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    vis = otree.visible_bruteforce(parent)
+    for layer in range(3):
+        q, k, v, ctx = synth.attention_inputs(w, layer, DEV, ctx_lens=[w.ctx, w.ctx - 100])
+        announce("attention reuse layer", layer)
+        out = api.tree_attention(q, k, v, ctx, w.ctx, t, ws=ws)
+        torch.cuda.synchronize()
+        ref = oattn.tree_attention(to64(q), to64(k), to64(v), ctx.tolist(), vis)
+        assert row_rel_err(to64(out), ref) <= TOL_BF16, layer
