@@ -195,7 +195,7 @@ def time_gpu(w, args):
     return ms_per_step, wall_s, stages_us, attn_call_us
 
 
-def cpu_baseline(w, n_layers, min_seconds=10.0, max_steps=5):
+def cpu_baseline(w, n_layers, min_seconds=10.0, max_steps=40):
     """The oracle as it stands (NumPy, fp64) on the host cores: whole steps of
     the same workload (attention on n_layers of the L layers, scaled to all
     L), repeated until about min_seconds of CPU work have been timed."""
@@ -281,7 +281,7 @@ def main():
     attn_total = stages_us["attention"]
     dominant_attention = attn_total >= stages_us["heads"]
     if dominant_attention:
-        roof = {"kernel": "tree_attn_bf16, one layer", "bound": "hbm",
+        roof = {"kernel": "tree attention, one layer (tree_attn_bf16 + merge_splits)", "bound": "hbm",
                 "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                 "bytes_per_launch": a_bytes, "us_per_launch": round(attn_us, 2)}

@@ -31,10 +31,9 @@
  *     same thread).  No exception crosses the ABI.
  *   - Scratch memory is passed in by the caller (ws, ws_bytes, sized by the
  *     matching *_workspace_size call, 256-byte aligned).  No call allocates
- *     device memory except medusa_tree_create.  Workspaces of
- *     medusa_tree_attention and of greedy medusa_accept_paths hold arrival
- *     counters: zero-fill them once before their first use; every call
- *     leaves them zero-filled again.
+ *     device memory except medusa_tree_create.  The workspace of greedy
+ *     medusa_accept_paths holds arrival counters: zero-fill it once before
+ *     its first use; every call leaves it zero-filled again.
  *   - Floating-point inputs must be finite.  Non-finite inputs give
  *     unspecified outputs, but every kernel still terminates and every index
  *     written stays in its documented range (or -1).
@@ -192,8 +191,10 @@ int medusa_tree_candidates(const float* head_logits, const int32_t* root,
  * scores, sums and accumulators; bf16 operands use MFMA.
  * Constraints: Hq % Hkv == 0; D = 128 (bf16) or D <= 128, D % 4 == 0 (f32);
  * T = the tree's T; S_cap >= ctx_max + T.  Pointers 16-byte aligned.
- * Workspace: split partials and one arrival counter per (b, K/V head, query
- * chunk); zero-filled before first use (0 bytes when no split is needed).
+ * Workspace: the split partials (unnormalised output, running max and sum
+ * of every query row per key split), merged by a second kernel on the same
+ * stream; 0 bytes when one split suffices.  Its contents need no
+ * initialisation, but calls that share a workspace must not overlap.
  * ------------------------------------------------------------------------ */
 size_t medusa_tree_attention_workspace_size(int B, int Hq, int Hkv, int D, int ctx_max,
                                             const medusa_tree_t* tree, medusa_dtype_t dt);

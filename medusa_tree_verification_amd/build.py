@@ -33,13 +33,18 @@ CFLAGS = [
 ]
 
 
+# per-source extra flags: the attention kernels never see a NaN (masked scores
+# are -inf, keys past a split read as zeros), so max() needs no NaN quieting
+EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, verbose: bool, resource_usage: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if resource_usage:
         cmd.append("-Rpass-analysis=kernel-resource-usage")
     if verbose:

@@ -9,31 +9,33 @@
 // merged afterwards.
 //
 // bf16 design (gfx950, D = 128)
-//   Work item: one workgroup (4 waves) per (sequence b, K/V head, query chunk,
-//   key split).  All T*G query rows of a K/V head (G = Hq/Hkv; row r = node
-//   r/G, query head r%G) go through the same pass over its keys, so every K/V
-//   byte of the split is read from HBM once.  The query tiles (16 rows) of
-//   the chunk are dealt round-robin to the 4 waves; every wave consumes every
-//   32-key block.
-//   Staging: the workgroup streams its key range in 32-key blocks (16 KB of
-//   K and V).  Each thread loads 64 bytes of every block into registers,
-//   three blocks ahead of use, then writes them to a ring of LDS slots: half
-//   the threads store K rows with their 16-byte chunks XOR-swizzled by key
-//   (conflict-free MFMA operand reads), the other half hold 4 keys x 8 d of V
-//   and store them transposed (rows = d, 4-key granules of 8 bytes, rows
-//   padded to 72 bytes, granules swizzled by (d/16)%8) -- the layout the
-//   P.V product needs.  One barrier per block; a slot is rewritten only
-//   after every wave has passed the barrier that follows its last use.
+//   Work item: one workgroup per (sequence b, K/V head, query chunk, key
+//   split).  All T*G query rows of a K/V head (G = Hq/Hkv; row r = node r/G,
+//   query head r%G) go through the same pass over its keys, so every K/V byte
+//   of the split is read from HBM once.  The workgroup has 12 waves in two
+//   roles that meet at one barrier per 64-key block:
+//   - 4 staging waves stream the split's K/V through buffer loads into
+//     registers, NREG blocks ahead of use, and write each block into one of
+//     two LDS slots: K rows padded to 272 bytes; V transposed (rows = d, 144
+//     bytes) with the 8 keys a lane feeds to one P.V MFMA k-step in one
+//     16-byte granule, granules XOR-swizzled by d/16.  Every LDS access of
+//     the kernel is free of bank conflicts.  Memory stalls of these waves do
+//     not hold up the arithmetic.
+//   - 8 compute waves: wave w takes query tiles (16 rows) w%4, w%4 + 4, ...
+//     and the 32-key half w/4 of every block, keeping its own online-softmax
+//     state; the two halves are merged through LDS at the end (fixed order).
 //   Scores: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows as the A
-//   operand, Q rows, staged once in LDS, as B; the d order is permuted the
-//   same way in both).  Lane l then holds query l%16 and 4 keys, so every
-//   lane's softmax state (max, sum, rescale) is its own query's.
+//   operand, Q rows as B -- in registers for one tile per wave, else staged
+//   in LDS; the d order is permuted the same way in both).  Lane l then holds
+//   query l%16 and 8 keys of the half, so every lane's softmax state (max,
+//   sum, rescale) is its own query's; the max over the lane rows uses the
+//   gfx950 permlane swaps (no LDS round trip).
 //   Values: O^T += V^T P^T; P^T comes straight from the score registers
-//   (packed to bf16) because the key order of the MFMA k-slots is chosen to
-//   match them.
+//   (packed to bf16) because the key order of the staged V^T granules is
+//   chosen to match them.
 //   Mask: context keys are always visible; tree key j is visible to node i
 //   iff bit j of node i's ancestor bitmask is set (rows staged in LDS); only
-//   blocks that reach past the context evaluate it.
+//   halves that reach past the context or the split evaluate it.
 //   exp2 with log2(e) folded into the scale; fp32 scores, sums and outputs.
 //   Splits: each workgroup writes its partial (unnormalised O, max, sum); a
 //   second kernel merges the splits of every row in split order (fixed
@@ -51,16 +53,19 @@ using namespace medusa::dev;
 namespace {
 
 constexpr int D = 128;
-constexpr int KB = 64;                  // keys per staged block
-constexpr int HALF = 32;                // keys per compute half (one P.V MFMA k-step)
-constexpr int VROWB = 72;               // bytes per V^T row (64 + 8 pad)
-constexpr int VT_BYTES = D * VROWB;     // one 32-key V^T tile: 9216
-constexpr int KROWB = D * 2;            // 256 bytes per K row
-constexpr int K_BYTES = KB * KROWB;     // 16384
-constexpr int SLOT_BYTES = K_BYTES + 2 * VT_BYTES;
-constexpr int QROW_CHUNKS = D / 8;      // 16-byte chunks per Q / K row
-constexpr int PREFETCH = 2;             // blocks in flight per workgroup (= LDS slots)
-constexpr int RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int KB = 64;                      // keys per block (one wave's unit of work)
+constexpr int GROWB = D * 2;                // bytes per K/V row in HBM
+constexpr int KROWB = GROWB + 16;           // K (and staged Q) row in LDS, padded: 272
+constexpr int K_TILE = KB * KROWB;          // 17408
+constexpr int VROWB = KB * 2 + 16;          // V^T row (one d, 64 keys) in LDS, padded: 144
+constexpr int V_TILE = D * VROWB;           // 18432
+constexpr int BLK_BYTES = K_TILE + V_TILE;  // 35840
+constexpr int NSLOT = 2;                    // LDS slots (blocks staged at once)
+constexpr int NREG = 2;                     // blocks in flight in staging registers
+constexpr int MERGE_BYTES = 8 * 64 * 16 + 64 * 8;  // one wave-tile's O, max and sum
+constexpr int MAX_SPLITS = 64;
+constexpr int LDS_MAX = 160 * 1024;         // LDS of one CU              // the merge keeps one split per lane
+constexpr int RSRC_WORD3 = 0x00020000;      // raw buffer, 32-bit data format
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -81,12 +86,6 @@ struct AttnArgs {
   int lds_mask, lds_q, lds_ring;  // dynamic LDS layout (byte offsets)
 };
 
-__device__ __forceinline__ float wave_max_16_32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
-}
-
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -100,13 +99,28 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-struct Stage {
-  uint4 k[4];  // 64 bytes of one K row
-  uint4 v[4];  // 4 keys x 8 d of V
-};
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// max / sum over the 4 lane rows (lanes l%16 + 16r) of a wave
+__device__ __forceinline__ float rows_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int QTW>
-__global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
+__global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
+  constexpr bool QREG = QTW == 1;  // Q fragments in registers, else in LDS
+  constexpr int ROWS_WG = 4 * QTW * 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int id = blockIdx.x;
   const int task = (id & 7) * a.per_xcd + (id >> 3);
@@ -120,7 +134,10 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool computes = wave < 8;  // waves 0-7 compute, waves 8-11 stage K/V
+  const int qw = wave & 3;         // query-tile lane of a compute wave
+  const int half = (wave >> 2) & 1;  // the 32-key half of every block it computes
   const int l16 = lane & 15;
   const int grp = lane >> 4;
 
@@ -131,88 +148,130 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
   const int k_end = (split == a.NS - 1) ? S : min(S, k_begin + a.chunk);
   const int nblk = k_end > k_begin ? (k_end - k_begin + KB - 1) / KB : 0;
 
-  // K/V of this (b, head) as buffer resources limited to the split's end:
+  // ---- staging roles: waves 8-9 load K rows, waves 10-11 V ----
+  const bool k_role = wave < 10;
+  const int rt = tid - (k_role ? 512 : 640);  // 0..127 within the role
+  const uint16_t* gbase = (k_role ? a.k : a.v) + static_cast<int64_t>(bh) * a.S_cap * D;
+  int goff[8];  // byte offsets of this thread's 8 loads within a block
+  int lds_w;    // this thread's LDS store offset within a slot
+  if (k_role) {
+    // chunk c = rt + 128*i of the block: key row c/16, 16-byte chunk c%16
+    const int base = (rt >> 4) * GROWB + (rt & 15) * 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) goff[i] = base + 8 * i * GROWB;
+    lds_w = (rt >> 4) * KROWB + (rt & 15) * 16;
+  } else {
+    // d-octet o of the 8 keys {4g..4g+3, 16+4g..16+4g+3} of half h
+    const int o = rt & 15, g = (rt >> 4) & 3, h = rt >> 6;
+    const int base = (h * 32 + 4 * g) * GROWB + o * 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) goff[i] = base + (i < 4 ? i : 12 + i) * GROWB;
+    lds_w = K_TILE + 8 * o * VROWB + 16 * ((h * 4 + g) ^ (o >> 1));
+  }
+  // a block's loads through a buffer resource that ends at the split's end:
   // reads of keys >= k_end return zeros (never the unused cache slots)
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.k + static_cast<int64_t>(bh) * a.S_cap * D), 0, k_end * KROWB, RSRC_WORD3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.v + static_cast<int64_t>(bh) * a.S_cap * D), 0, k_end * KROWB, RSRC_WORD3);
-
-  // staging roles (every thread): K row tid/4, 16-byte chunks 4*(tid%4)..+3;
-  // V keys 4*(tid/16)..+3 at d-octet tid%16
-  const int k_row = tid >> 2, k_ch = (tid & 3) * 4;
-  const int v_quad = tid >> 4, v_oct = tid & 15;
-  auto gload = [&](Stage& st, int blk) __attribute__((always_inline)) {
+  auto gload = [&](uint4 (&x)[8], int blk) __attribute__((always_inline)) {
     const int kb = k_begin + blk * KB;
-    const int ko = (kb + k_row) * KROWB + k_ch * 16;
+    const int nrec = (k_end - kb) * GROWB;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(gbase + static_cast<int64_t>(kb) * D), 0, nrec > 0 ? nrec : 0,
+        RSRC_WORD3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.k[i] = bload16(rk, ko + 16 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.v[i] = bload16(rv, (kb + 4 * v_quad + i) * KROWB + v_oct * 16);
+    for (int i = 0; i < 8; ++i) x[i] = bload16(r, goff[i]);
   };
-  auto lds_put = [&](const Stage& st, char* slot) __attribute__((always_inline)) {
-    uint4* row = reinterpret_cast<uint4*>(slot + k_row * KROWB);
+  auto lds_put = [&](const uint4 (&x)[8], char* slot) __attribute__((always_inline)) {
+    char* p = slot + lds_w;
+    if (k_role) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) row[(k_ch + i) ^ (k_row & 15)] = st.k[i];
-    // V: 4 keys x 8 d -> 8 granules (4 keys of one d) of this half's V^T tile
-    char* vt = slot + K_BYTES + (v_quad >> 3) * VT_BYTES;
-    const int qd = v_quad & 7;
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(p + 8 * i * KROWB) = x[i];
+    } else {
+      // row d = 8o + dd of V^T: element dd of each of the 8 keys, in k-slot order
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * v_oct + e;
-      const uint32_t a0 = reinterpret_cast<const uint32_t*>(&st.v[0])[e >> 1];
-      const uint32_t a1 = reinterpret_cast<const uint32_t*>(&st.v[1])[e >> 1];
-      const uint32_t a2 = reinterpret_cast<const uint32_t*>(&st.v[2])[e >> 1];
-      const uint32_t a3 = reinterpret_cast<const uint32_t*>(&st.v[3])[e >> 1];
-      uint32_t w0, w1;
-      if ((e & 1) == 0) {
-        w0 = (a0 & 0xffffu) | (a1 << 16);
-        w1 = (a2 & 0xffffu) | (a3 << 16);
-      } else {
-        w0 = (a0 >> 16) | (a1 & 0xffff0000u);
-        w1 = (a2 >> 16) | (a3 & 0xffff0000u);
+      for (int dd = 0; dd < 8; ++dd) {
+        const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+        uint4 w;
+        w.x = __builtin_amdgcn_perm(word(x[1], dd >> 1), word(x[0], dd >> 1), sel);
+        w.y = __builtin_amdgcn_perm(word(x[3], dd >> 1), word(x[2], dd >> 1), sel);
+        w.z = __builtin_amdgcn_perm(word(x[5], dd >> 1), word(x[4], dd >> 1), sel);
+        w.w = __builtin_amdgcn_perm(word(x[7], dd >> 1), word(x[6], dd >> 1), sel);
+        *reinterpret_cast<uint4*>(p + dd * VROWB) = w;
       }
-      *reinterpret_cast<uint2*>(vt + d * VROWB + ((qd ^ ((d >> 4) & 7)) * 8)) = make_uint2(w0, w1);
     }
   };
 
-  // ---- prologue: Q rows and mask rows first, then the first blocks ----
-  constexpr int ROWS_WG = 4 * QTW * 16;
-  constexpr int Q_PER_THREAD = ROWS_WG * QROW_CHUNKS / 256;  // 4 * QTW
-  const int row0 = qc * ROWS_WG;
-  uint4 qv[Q_PER_THREAD];
-#pragma unroll
-  for (int u = 0; u < Q_PER_THREAD; ++u) {
-    const int idx = tid + 256 * u;
-    const int rr = idx / QROW_CHUNKS, ch = idx % QROW_CHUNKS;
-    const int r = min(row0 + rr, a.QR - 1);
-    const int node = r / a.G, gq = r % a.G;
-    qv[u] = ldg16(a.q + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + ch * 8);
-  }
-  const int nmask = a.T * a.W;
-  uint64_t mv[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) mv[u] = (tid + 256 * u < nmask) ? a.mask[tid + 256 * u] : 0ull;
-  Stage s0, s1;
-  if (nblk > 0) gload(s0, 0);
-  if (nblk > 1) gload(s1, 1);
-  uint4* sq = reinterpret_cast<uint4*>(smem + a.lds_q);
-#pragma unroll
-  for (int u = 0; u < Q_PER_THREAD; ++u) {
-    const int idx = tid + 256 * u;
-    const int rr = idx / QROW_CHUNKS, ch = idx % QROW_CHUNKS;
-    sq[rr * QROW_CHUNKS + (ch ^ (rr & 15))] = (row0 + rr < a.QR) ? qv[u] : make_uint4(0, 0, 0, 0);
-  }
-  uint64_t* smask = reinterpret_cast<uint64_t*>(smem + a.lds_mask);
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (tid + 256 * u < nmask) smask[tid + 256 * u] = mv[u];
+  char* ring = smem + a.lds_ring;
 
-  // this wave's query tiles: wave, wave + 4, ...
+  // ---- staging waves: stream K/V into the LDS ring, one block per barrier ----
+  // Every global load here is issued unconditionally (a block past the
+  // split's end reads zeros through its empty buffer resource), and this
+  // path never joins the compute waves' code, so the loads in flight are the
+  // same on every path and each wait covers exactly the block it needs.
+  // Pipeline: while the compute waves work on block i from its LDS slot,
+  // these waves write block i+1 (from registers) into the other slot and
+  // refill those registers with block i+1+NREG.  A slot is rewritten only
+  // after the barrier that follows its last reader.  Both roles pass the
+  // same number of barriers.
+  if (!computes) {
+    uint4 R[NREG][8];  // blocks loaded but not yet in LDS
+#pragma unroll
+    for (int j = 0; j < NREG; ++j) {
+      gload(R[j], j);
+      __builtin_amdgcn_sched_barrier(0);  // keep the blocks' loads in order
+    }
+    if (nblk > 0) lds_put(R[0], ring);
+    gload(R[0], NREG);
+    __syncthreads();
+    for (int blk = 0; blk < nblk; blk += NREG) {
+#pragma unroll
+      for (int j = 0; j < NREG; ++j) {
+        if (blk + j + 1 < nblk) lds_put(R[(j + 1) % NREG], ring + ((blk + j + 1) & 1) * BLK_BYTES);
+        gload(R[(j + 1) % NREG], blk + j + 1 + NREG);
+        __syncthreads();
+      }
+    }
+    __syncthreads();  // the compute waves' merge of the two key halves
+    return;
+  }
+
+  // ---- compute waves ----
+  // Q and the mask rows (the staging waves' only
+  // global loads are K/V)
+  const int row0 = qc * ROWS_WG;
+  auto q_ptr = [&](int r, int ch) __attribute__((always_inline)) {
+    const int node = r / a.G, gq = r % a.G;
+    return a.q + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + ch * 8;
+  };
+  bf16x8 qf[QREG ? 4 : 1];
+  uint64_t* smask = reinterpret_cast<uint64_t*>(smem + a.lds_mask);
+  {
+    if constexpr (QREG) {
+      const int r = min(row0 + qw * 16 + l16, a.QR - 1);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(ldg16(q_ptr(r, grp * 4 + s)));
+    } else {
+      constexpr int Q_PER_THREAD = ROWS_WG * 16 / 512;
+#pragma unroll
+      for (int u = 0; u < Q_PER_THREAD; ++u) {
+        const int idx = tid + 512 * u;
+        const uint4 v = ldg16(q_ptr(min(row0 + idx / 16, a.QR - 1), idx % 16));
+        *reinterpret_cast<uint4*>(smem + a.lds_q + (idx / 16) * KROWB + (idx % 16) * 16) =
+            (row0 + idx / 16 < a.QR) ? v : make_uint4(0, 0, 0, 0);
+      }
+    }
+    const int nmask = a.T * a.W;  // <= 1024
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint64_t mv = a.mask[min(tid + 512 * u, nmask - 1)];
+      if (tid + 512 * u < nmask) smask[tid + 512 * u] = mv;
+    }
+  }
+  const uint32_t* smask32 = reinterpret_cast<const uint32_t*>(smask);
+
+  // compute-wave state: this wave's query tiles qw, qw + 4, ...
   int qnode[QTW];
 #pragma unroll
   for (int t = 0; t < QTW; ++t) {
-    const int r = row0 + (wave + 4 * t) * 16 + l16;
+    const int r = row0 + (qw + 4 * t) * 16 + l16;
     qnode[t] = r < a.QR ? r / a.G : 0;
   }
   f32x4 o[QTW][8];
@@ -224,44 +283,48 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  char* ring = smem + a.lds_ring;
+  const char* sq = smem + a.lds_q + l16 * KROWB + grp * 64;
+  // V^T read offsets: granule (4h + grp) ^ dt of row dt*16 + l16
+  int vx[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) vx[c] = K_TILE + l16 * VROWB + 16 * (grp ^ c);
 
-  // one 32-key half of a staged block
-  auto compute_half = [&](const char* slot, int h, int kb) __attribute__((always_inline)) {
-    bf16x8 kf[2][4];
+  // this wave's 32-key half of a 64-key block (keys kh .. kh+31)
+  auto compute = [&](const char* blk, int kh) __attribute__((always_inline)) {
+    f32x4 sc[QTW][2];
+    const char* kr = blk + (half * 32 + l16) * KROWB + grp * 64;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const uint4* row = reinterpret_cast<const uint4*>(slot + (h * HALF + st * 16 + l16) * KROWB);
+      bf16x8 kf[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) kf[st][s] = as_bf16x8(row[(grp * 4 + s) ^ l16]);
-    }
-    f32x4 sc[2][QTW];
+      for (int s = 0; s < 4; ++s)
+        kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + st * 16 * KROWB + 16 * s));
 #pragma unroll
-    for (int t = 0; t < QTW; ++t) {
-      const uint4* qrow = sq + ((wave + 4 * t) * 16 + l16) * QROW_CHUNKS;
-      f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < QTW; ++t) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 qf = as_bf16x8(qrow[(grp * 4 + s) ^ l16]);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][s], qf, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][s], qf, acc1, 0, 0, 0);
+        for (int s = 0; s < 4; ++s) {
+          bf16x8 q;
+          if constexpr (QREG) q = qf[s];
+          else q = as_bf16x8(*reinterpret_cast<const uint4*>(sq + (qw + 4 * t) * 16 * KROWB + 16 * s));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], q, acc, 0, 0, 0);
+        }
+        sc[t][st] = acc;
       }
-      sc[0][t] = acc0 * a.scale_log2;
-      sc[1][t] = acc1 * a.scale_log2;
     }
-    if (kb + HALF > ctx || kb + HALF > k_end) {  // the tree region or the split's end
+    if (kh + 32 > ctx || kh + 32 > k_end) {  // the tree region or the split's end
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int key = kb + st * 16 + 4 * grp + e;
+          const int key = kh + st * 16 + 4 * grp + e;
           const int jj = key - ctx;
+          const int jc = jj < 0 ? 0 : (jj >= a.T ? a.T - 1 : jj);
 #pragma unroll
           for (int t = 0; t < QTW; ++t) {
-            bool vis = key < k_end;
-            if (vis && jj >= 0) vis = (smask[qnode[t] * a.W + (jj >> 6)] >> (jj & 63)) & 1ull;
-            if (!vis) sc[st][t][e] = -INFINITY;
+            const uint32_t wv = smask32[qnode[t] * 2 * a.W + (jc >> 5)];
+            const bool vis = key < k_end && (jj < 0 || ((wv >> (jc & 31)) & 1u));
+            if (!vis) sc[t][st][e] = -INFINITY;
           }
         }
       }
@@ -269,78 +332,86 @@ __global__ __launch_bounds__(256) void tree_attn_bf16(AttnArgs a) {
     uint4 pb[QTW];
 #pragma unroll
     for (int t = 0; t < QTW; ++t) {
-      float bm = fmaxf(fmaxf(fmaxf(sc[0][t][0], sc[0][t][1]), fmaxf(sc[0][t][2], sc[0][t][3])),
-                       fmaxf(fmaxf(sc[1][t][0], sc[1][t][1]), fmaxf(sc[1][t][2], sc[1][t][3])));
-      bm = wave_max_16_32(bm);
-      const float mnew = fmaxf(m_run[t], bm);
+      float mx = fmaxf(fmaxf(fmaxf(sc[t][0][0], sc[t][0][1]), fmaxf(sc[t][0][2], sc[t][0][3])),
+                       fmaxf(fmaxf(sc[t][1][0], sc[t][1][1]), fmaxf(sc[t][1][2], sc[t][1][3])));
+      mx = rows_max(mx);
+      const float mnew = fmaxf(m_run[t], mx * a.scale_log2);
       const float muse = (mnew == -INFINITY) ? 0.f : mnew;
       const float alpha = __builtin_amdgcn_exp2f(m_run[t] - muse);
       m_run[t] = mnew;
-      float p[8];
+      float p[2][4];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[st * 4 + e] = __builtin_amdgcn_exp2f(sc[st][t][e] - muse);
-      l_run[t] = l_run[t] * alpha + ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      pb[t] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                         pack_bf16(p[6], p[7]));
+        for (int e = 0; e < 4; ++e) p[st][e] = __builtin_amdgcn_exp2f(fmaf(sc[t][st][e], a.scale_log2, -muse));
+      l_run[t] = fmaf(l_run[t], alpha, ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                                           ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
+      pb[t] = make_uint4(pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
+                         pack_bf16(p[1][2], p[1][3]));
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // some query's max moved
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
       }
     }
-    const char* vt = slot + K_BYTES + h * VT_BYTES;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const char* rowp = vt + (dt * 16 + l16) * VROWB;
-      const uint2 lo = *reinterpret_cast<const uint2*>(rowp + ((grp ^ (dt & 7)) * 8));
-      const uint2 hi = *reinterpret_cast<const uint2*>(rowp + (((grp + 4) ^ (dt & 7)) * 8));
-      const bf16x8 va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const bf16x8 va = as_bf16x8(*reinterpret_cast<const uint4*>(
+          blk + vx[dt & 3] + dt * 16 * VROWB + 64 * ((half ^ (dt >> 2)) & 1)));
 #pragma unroll
       for (int t = 0; t < QTW; ++t)
         o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(pb[t]), o[t][dt], 0, 0, 0);
     }
   };
 
-  // Pipeline: block 0 is staged before the loop; step i computes block i from
-  // its slot while staging block i+1 into the other slot and refilling that
-  // register buffer with block i+1+PREFETCH; one barrier per step.  A slot is
-  // rewritten only after the barrier that follows its last reader.
-  if (nblk > 0) {
-    lds_put(s0, ring);
-    if (PREFETCH < nblk) gload(s0, PREFETCH);
+  __syncthreads();
+  for (int blk = 0; blk < nblk; blk += NREG) {
+#pragma unroll
+    for (int j = 0; j < NREG; ++j) {
+      const int kh = k_begin + (blk + j) * KB + 32 * half;
+      if (blk + j < nblk && kh < k_end) compute(ring + ((blk + j) & 1) * BLK_BYTES, kh);
+      __syncthreads();
+    }
+  }
+
+  // full per-query sums (each lane row holds a quarter of the keys)
+#pragma unroll
+  for (int t = 0; t < QTW; ++t) l_run[t] = rows_sum(l_run[t]);
+
+  // the second-half waves hand their state to the first-half waves through
+  // LDS (Q and the ring are free after the loop's last barrier)
+  auto region = [&](int t) __attribute__((always_inline)) {
+    return smem + a.lds_q + (qw * QTW + t) * MERGE_BYTES;
+  };
+  if (half == 1) {
+#pragma unroll
+    for (int t = 0; t < QTW; ++t) {
+      char* r = region(t);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) reinterpret_cast<f32x4*>(r)[dt * 64 + lane] = o[t][dt];
+      reinterpret_cast<float2*>(r + 8 * 64 * 16)[lane] = make_float2(m_run[t], l_run[t]);
+    }
   }
   __syncthreads();
-  auto step = [&](int blk, Stage& next, int si_cur, int si_next) __attribute__((always_inline)) {
-    const char* cur = ring + si_cur * SLOT_BYTES;
-    const int kb = k_begin + blk * KB;
-    compute_half(cur, 0, kb);
-    if (kb + HALF < k_end) compute_half(cur, 1, kb + HALF);
-    if (blk + 1 < nblk) {
-      lds_put(next, ring + si_next * SLOT_BYTES);
-      if (blk + 1 + PREFETCH < nblk) gload(next, blk + 1 + PREFETCH);
-    }
-    __syncthreads();
-  };
-  int blk = 0;
-  for (; blk + 2 <= nblk; blk += 2) {
-    step(blk, s1, 0, 1);
-    step(blk + 1, s0, 1, 0);
-  }
-  if (blk < nblk) step(blk, s1, 0, 1);
-
-  // full per-query sums (each lane group holds a quarter of the keys)
+  if (half == 1) return;
 #pragma unroll
   for (int t = 0; t < QTW; ++t) {
-    l_run[t] += __shfl_xor(l_run[t], 16, 64);
-    l_run[t] += __shfl_xor(l_run[t], 32, 64);
+    const char* r = region(t);
+    const float2 ml = reinterpret_cast<const float2*>(r + 8 * 64 * 16)[lane];
+    const float M = fmaxf(m_run[t], ml.x);
+    const float muse = (M == -INFINITY) ? 0.f : M;
+    const float a0 = __builtin_amdgcn_exp2f(m_run[t] - muse);
+    const float a1 = __builtin_amdgcn_exp2f(ml.x - muse);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[t][dt] = o[t][dt] * a0 + reinterpret_cast<const f32x4*>(r)[dt * 64 + lane] * a1;
+    l_run[t] = l_run[t] * a0 + ml.y * a1;
+    m_run[t] = M;
   }
 
   // ---- one split: the output; several: this split's partial ----
   const int BH = a.B * a.Hkv;
 #pragma unroll
   for (int t = 0; t < QTW; ++t) {
-    const int r = row0 + (wave + 4 * t) * 16 + l16;
+    const int r = row0 + (qw + 4 * t) * 16 + l16;
     if (r >= a.QR) continue;
     if (a.NS == 1) {
       const float inv = 1.0f / l_run[t];
@@ -494,25 +565,38 @@ int cu_count() {
 const void* kernel_for(int qtw) {
   switch (qtw) {
     case 1: return reinterpret_cast<const void*>(&tree_attn_bf16<1>);
-    case 2: return reinterpret_cast<const void*>(&tree_attn_bf16<2>);
-    case 3: return reinterpret_cast<const void*>(&tree_attn_bf16<3>);
-    default: return reinterpret_cast<const void*>(&tree_attn_bf16<4>);
+    default: return reinterpret_cast<const void*>(&tree_attn_bf16<2>);
   }
+}
+
+// Above 64 KiB the dynamic LDS size must be allowed for each kernel (the
+// attribute must not exceed what the kernel can use, so it is set to the
+// largest size asked for so far).
+int allow_lds(int qtw, int lds) {
+  static int allowed[4] = {0};
+  if (lds <= 64 * 1024 || lds <= allowed[qtw]) return MEDUSA_OK;
+  const hipError_t e = hipFuncSetAttribute(kernel_for(qtw), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    set_error("cannot allow %d bytes of dynamic LDS for tree attention: %s", lds, hipGetErrorString(e));
+    return MEDUSA_EUNSUPPORTED;
+  }
+  allowed[qtw] = lds;
+  return MEDUSA_OK;
 }
 
 // workgroups of this configuration one CU runs at once (1 if unknown)
 int occupancy(int qtw, int lds) {
-  static int cache[5][8] = {{0}};
+  static int cache[4][9] = {{0}};
   const int bucket = lds / (20 * 1024);
-  if (bucket < 8 && cache[qtw][bucket]) return cache[qtw][bucket];
+  if (bucket < 9 && cache[qtw][bucket]) return cache[qtw][bucket];
   int n = 0;
-  if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(kernel_for(qtw), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel_for(qtw), 256, lds) != hipSuccess || n < 1) {
+  if (allow_lds(qtw, lds) != MEDUSA_OK ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel_for(qtw), 768, lds) != hipSuccess || n < 1) {
     (void)hipGetLastError();
     n = 1;
   }
-  if (bucket < 8) cache[qtw][bucket] = n;
+  if (bucket < 9) cache[qtw][bucket] = n;
   return n;
 }
 
@@ -521,35 +605,38 @@ Plan make_plan(int B, int Hq, int Hkv, int ctx_max, int T, int W) {
   p.G = Hq / Hkv;
   p.QR = T * p.G;
   p.NQT = (p.QR + 15) / 16;
-  p.QTW = (p.NQT + 3) / 4;
-  if (p.QTW > 4) p.QTW = 4;
-  p.QC = (p.NQT + 4 * p.QTW - 1) / (4 * p.QTW);
+  // at most 2 query tiles per compute wave (more would spill registers)
+  p.QC = (p.NQT + 7) / 8;
+  p.QTW = (p.NQT + 4 * p.QC - 1) / (4 * p.QC);
   p.QRpad = p.NQT * 16;
   p.lds_mask = 0;
   p.lds_q = static_cast<int>(round_up(static_cast<size_t>(T) * W * 8, 16));
-  p.lds_ring = p.lds_q + 4 * p.QTW * 16 * D * 2;
-  p.lds_bytes = p.lds_ring + PREFETCH * SLOT_BYTES;
+  p.lds_ring = p.lds_q + (p.QTW == 1 ? 0 : 4 * p.QTW * 16 * KROWB);
+  p.lds_bytes = p.lds_ring + NSLOT * BLK_BYTES;
   const int Smax = ctx_max + T;
   const int base = B * Hkv * p.QC;
   int ns = env_int("MEDUSA_ATTN_SPLITS", 0);
   if (ns <= 0) {
-    // pick the split count minimising rounds x (fixed cost + keys per split),
-    // counting the workgroups all CUs hold at once
+    // pick the split count minimising rounds x (fixed cost + blocks per
+    // split) + a cost per split (its partial is written, merged and read),
+    // counting the workgroups all CUs hold at once; in units of one block
     const int slots = cu_count() * occupancy(p.QTW, p.lds_bytes);
-    const double fixed_keys = 96.0;  // per-workgroup latency, in key-times
+    const double fixed_blocks = 1.5;  // prologue and epilogue
+    const double per_split = 0.5;
     double best = 1e300;
     ns = 1;
-    const int max_ns = (Smax + KB - 1) / KB;  // >= one staged block per split
-    for (int n = 1; n <= max_ns && n <= 64; ++n) {
+    const int max_ns = (Smax + KB - 1) / KB;  // >= one block per split
+    for (int n = 1; n <= max_ns && n <= MAX_SPLITS; ++n) {
       const int rounds = (base * n + slots - 1) / slots;
-      const double t = rounds * (fixed_keys + std::ceil(static_cast<double>(Smax) / n));
+      const int blocks = (Smax + n * KB - 1) / (n * KB);
+      const double t = rounds * (fixed_blocks + blocks) + (n > 1 ? per_split * n : 0.0);
       if (t < best * 0.999) {
         best = t;
         ns = n;
       }
     }
   }
-  if (ns > 64) ns = 64;  // the merge keeps one split per lane
+  if (ns > MAX_SPLITS) ns = MAX_SPLITS;
   int chunk = (Smax + ns - 1) / ns;
   chunk = (chunk + KB - 1) / KB * KB;
   p.chunk = chunk;
@@ -565,22 +652,9 @@ Plan make_plan(int B, int Hq, int Hkv, int ctx_max, int T, int W) {
 
 template <int QTW>
 int launch_cfg(const AttnArgs& a, int grid, int lds, hipStream_t s) {
-  if (lds > 64 * 1024) {
-    // above 64 KiB the dynamic LDS size must be allowed explicitly
-    static int allowed = 0;
-    if (lds > allowed) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tree_attn_bf16<QTW>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (e != hipSuccess) {
-        (void)hipGetLastError();
-        set_error("cannot allow %d bytes of dynamic LDS for tree attention: %s", lds,
-                  hipGetErrorString(e));
-        return MEDUSA_EUNSUPPORTED;
-      }
-      allowed = lds;
-    }
-  }
-  hipLaunchKernelGGL((tree_attn_bf16<QTW>), dim3(grid), dim3(256), lds, s, a);
+  const int rc = allow_lds(QTW, lds);
+  if (rc) return rc;
+  hipLaunchKernelGGL((tree_attn_bf16<QTW>), dim3(grid), dim3(768), lds, s, a);
   return check_launch("tree attention (bf16)");
 }
 
@@ -642,13 +716,14 @@ extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const v
     set_error("bf16 tree attention supports D = 128 (got D=%d)", D_);
     return MEDUSA_EUNSUPPORTED;
   }
+  MEDUSA_CHECK_ARG(S_cap < (1 << 23), "S_cap=%d too large (K/V byte offsets are 32-bit)", S_cap);
   const Plan p = make_plan(B, Hq, Hkv, ctx_max, tree->T, tree->W);
   if (p.NS > 1 && (!ws || ws_bytes < p.ws_bytes || !aligned256(ws))) {
     set_error("tree attention workspace: need %zu bytes, 256-byte aligned (got %zu at %p)",
               p.ws_bytes, ws_bytes, ws);
     return MEDUSA_EWORKSPACE;
   }
-  if (p.lds_bytes > 160 * 1024) {
+  if (p.lds_bytes > LDS_MAX) {
     set_error("tree attention needs %d bytes of LDS (T=%d too large)", p.lds_bytes, tree->T);
     return MEDUSA_EUNSUPPORTED;
   }
@@ -685,9 +760,7 @@ extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const v
   const int grid = 8 * a.per_xcd;
   switch (p.QTW) {
     case 1: rc = launch_cfg<1>(a, grid, p.lds_bytes, stream); break;
-    case 2: rc = launch_cfg<2>(a, grid, p.lds_bytes, stream); break;
-    case 3: rc = launch_cfg<3>(a, grid, p.lds_bytes, stream); break;
-    default: rc = launch_cfg<4>(a, grid, p.lds_bytes, stream); break;
+    default: rc = launch_cfg<2>(a, grid, p.lds_bytes, stream); break;
   }
   if (rc || p.NS == 1) return rc;
   const int64_t rows = static_cast<int64_t>(B) * Hkv * p.QR;

@@ -116,6 +116,24 @@ def test_attention_full_size_sampled_rows(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("splits", [19, 63])
+def test_attention_many_splits(splits, monkeypatch):
+    """Many splits per (sequence, head), repeated on one workspace."""
+    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=2, Hq=8, Hkv=4, ctx=4100, cfg_id=235)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    t = api.Tree(parent, rank, w.topk)
+    q, k, v, ctx = synth.attention_inputs(w, 0, DEV, ctx_lens=[4100, 2600])
+    monkeypatch.setenv("MEDUSA_ATTN_SPLITS", str(splits))
+    announce("attention many splits", splits)
+    nb = api.tree_attention_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.ctx, t, torch.bfloat16)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    ref = _oracle_full(q, k, v, ctx.tolist(), parent)
+    for rep in range(3):
+        out = api.tree_attention(q, k, v, ctx, w.ctx, t, ws=ws)
+        torch.cuda.synchronize()
+        assert row_rel_err(to64(out), ref) <= TOL_BF16, rep
+
+
 def test_attention_deterministic():
     w = synth.WORKLOADS["zephyr7b-shaped"].scaled(B=2, ctx=1000, cfg_id=240)
     parent, rank = synth.cost_ordered_tree(w.topk, w.T)
@@ -151,7 +169,7 @@ def test_attention_argument_errors():
 
 def test_attention_workspace_reused_across_calls():
     """Consecutive calls sharing one workspace (as the layers of a step do):
-    the arrival counters must come back to zero after every call."""
+    no call may see another call's split partials."""
     w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=2, Hq=8, Hkv=4, ctx=1500, cfg_id=260)
     parent, rank = synth.cost_ordered_tree(w.topk, w.T)
     t = api.Tree(parent, rank, w.topk)
