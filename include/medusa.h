@@ -191,9 +191,10 @@ int medusa_tree_candidates(const float* head_logits, const int32_t* root,
  * scores, sums and accumulators; bf16 operands use MFMA.
  * Constraints: Hq % Hkv == 0; D = 128 (bf16) or D <= 128, D % 4 == 0 (f32);
  * T = the tree's T; S_cap >= ctx_max + T.  Pointers 16-byte aligned.
- * Workspace: the split partials (unnormalised output, running max and sum
- * of every query row per key split), merged by a second kernel on the same
- * stream; 0 bytes when one split suffices.  Its contents need no
+ * Workspace: the split partials (every query row's output over one key
+ * split, normalised by its own exp-sum, in bf16, plus that split's max and
+ * exp-sum in fp32), merged by a second kernel on the same stream; 0 bytes
+ * when one split suffices.  Its contents need no
  * initialisation, but calls that share a workspace must not overlap.
  * ------------------------------------------------------------------------ */
 size_t medusa_tree_attention_workspace_size(int B, int Hq, int Hkv, int D, int ctx_max,

@@ -37,9 +37,9 @@
 //   iff bit j of node i's ancestor bitmask is set (rows staged in LDS); only
 //   halves that reach past the context or the split evaluate it.
 //   exp2 with log2(e) folded into the scale; fp32 scores, sums and outputs.
-//   Splits: each workgroup writes its partial (unnormalised O, max, sum); a
-//   second kernel merges the splits of every row in split order (fixed
-//   order: deterministic).  Workgroups are numbered so that all splits of one
+//   Splits: each workgroup writes its partial (its output normalised by its
+//   own sum, in bf16, and the max and sum in fp32); a second kernel merges
+//   the splits of every row in split order (fixed order: deterministic).  Workgroups are numbered so that all splits of one
 //   (b, K/V head) land on the same XCD (dispatch assigns workgroup i to XCD
 //   i % 8), which keeps their partials in one L2.
 #include <cmath>
@@ -81,8 +81,8 @@ struct AttnArgs {
   int tasks, per_xcd;
   float scale_log2;
   uint16_t* out;
-  float* part_o;   // [NS][B*Hkv][QRpad][D]
-  float* part_ml;  // [NS][B*Hkv][QRpad][2]
+  uint16_t* part_o;  // [NS][B*Hkv][QRpad][D] bf16, normalised (O / sum)
+  float* part_ml;    // [NS][B*Hkv][QRpad][2] fp32 (max, sum)
   int lds_mask, lds_q, lds_ring;  // dynamic LDS layout (byte offsets)
 };
 
@@ -424,61 +424,74 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
             make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
       }
     } else {
+      // the split's output normalised by its own sum (bf16), with its max and
+      // sum in fp32; a split that saw no key has sum 0 and writes zeros
       const int64_t prow = (static_cast<int64_t>(split) * BH + bh) * a.QRpad + r;
-      float* po = a.part_o + prow * D;
+      uint16_t* po = a.part_o + prow * D;
+      const float inv = l_run[t] > 0.f ? 1.0f / l_run[t] : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = o[t][dt];
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 v = o[t][dt] * inv;
+        *reinterpret_cast<uint2*>(po + dt * 16 + 4 * grp) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+      }
       if (grp == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_run[t], l_run[t]);
     }
   }
 }
 
-// Merge the NS split partials of every query row, in split order (NS <= 64).
-// One wave per row, 2 consecutive d per lane; every split's (max, sum) and
-// output values are requested before any arithmetic (one round trip).
+// Merge the NS split partials of every query row, in split order (NS <= 64):
+// out = sum_s w_s l_s O_s / sum_s w_s l_s with w_s = exp2(m_s - max_s m_s) and
+// O_s the split's normalised output.  Two rows per wave, 32 lanes per row,
+// 4 consecutive d per lane; every split's (max, sum) and output values are
+// requested before any arithmetic (one round trip).
 __global__ __launch_bounds__(256) void merge_splits(AttnArgs a) {
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 31;  // lane within the row's half-wave
   const int BH = a.B * a.Hkv;
-  const int64_t gr = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (gr >= static_cast<int64_t>(BH) * a.QR) return;
-  const int bh = static_cast<int>(gr / a.QR);
-  const int r = static_cast<int>(gr % a.QR);
+  const int64_t gr = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const bool live = gr < static_cast<int64_t>(BH) * a.QR;  // both halves reach the shuffles
+  const int64_t grc = live ? gr : 0;
+  const int bh = static_cast<int>(grc / a.QR);
+  const int r = static_cast<int>(grc % a.QR);
   const int64_t stride = static_cast<int64_t>(BH) * a.QRpad;  // rows between splits
   const int64_t row = static_cast<int64_t>(bh) * a.QRpad + r;
   const int ns = a.NS;
-  float2 ml = make_float2(-INFINITY, 0.f);
-  if (lane < ns) ml = *reinterpret_cast<const float2*>(a.part_ml + (lane * stride + row) * 2);
-  float2 ov[16];
+  // lane s holds splits s and s + 32
+  float2 ml0 = make_float2(-INFINITY, 0.f), ml1 = make_float2(-INFINITY, 0.f);
+  if (lane < ns) ml0 = *reinterpret_cast<const float2*>(a.part_ml + (lane * stride + row) * 2);
+  if (lane + 32 < ns) ml1 = *reinterpret_cast<const float2*>(a.part_ml + ((lane + 32) * stride + row) * 2);
+  uint2 ov[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u)
-    ov[u] = (u < ns) ? *reinterpret_cast<const float2*>(a.part_o + (u * stride + row) * D + 2 * lane)
-                     : make_float2(0.f, 0.f);
-  float M = ml.x;
+    ov[u] = (u < ns) ? *reinterpret_cast<const uint2*>(a.part_o + (u * stride + row) * D + 4 * lane)
+                     : make_uint2(0, 0);
+  float M = fmaxf(ml0.x, ml1.x);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  for (int off = 16; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 32));
   const float muse = (M == -INFINITY) ? 0.f : M;
-  const float w = __builtin_amdgcn_exp2f(ml.x - muse);  // lane s: weight of split s
-  float L = ml.y * w;
+  const float w0 = __builtin_amdgcn_exp2f(ml0.x - muse) * ml0.y;  // weight of split lane
+  const float w1 = __builtin_amdgcn_exp2f(ml1.x - muse) * ml1.y;  // weight of split lane + 32
+  float L = w0 + w1;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
-  float o0 = 0.f, o1 = 0.f;
+  for (int off = 16; off >= 1; off >>= 1) L += __shfl_xor(L, off, 32);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  auto add = [&](uint2 v, float wu) __attribute__((always_inline)) {
+    acc[0] = fmaf(bf16_bits_to_f32(v.x & 0xffffu), wu, acc[0]);
+    acc[1] = fmaf(bf16_bits_to_f32(v.x >> 16), wu, acc[1]);
+    acc[2] = fmaf(bf16_bits_to_f32(v.y & 0xffffu), wu, acc[2]);
+    acc[3] = fmaf(bf16_bits_to_f32(v.y >> 16), wu, acc[3]);
+  };
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const float wu = __shfl(w, u, 64);
-    o0 = fmaf(ov[u].x, wu, o0);
-    o1 = fmaf(ov[u].y, wu, o1);
+  for (int u = 0; u < 16; ++u) add(ov[u], __shfl(w0, u, 32));
+  for (int s_ = 16; s_ < ns; ++s_) {
+    const uint2 v = *reinterpret_cast<const uint2*>(a.part_o + (s_ * stride + row) * D + 4 * lane);
+    add(v, s_ < 32 ? __shfl(w0, s_, 32) : __shfl(w1, s_ - 32, 32));
   }
-  for (int s = 16; s < ns; ++s) {
-    const float2 v = *reinterpret_cast<const float2*>(a.part_o + (s * stride + row) * D + 2 * lane);
-    const float wu = __shfl(w, s, 64);
-    o0 = fmaf(v.x, wu, o0);
-    o1 = fmaf(v.y, wu, o1);
-  }
+  if (!live) return;
   const float inv = 1.0f / L;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int node = r / a.G, gq = r % a.G;
-  uint16_t* op = a.out + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + 2 * lane;
-  *reinterpret_cast<uint32_t*>(op) = pack_bf16(o0 * inv, o1 * inv);
+  uint16_t* op = a.out + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + 4 * lane;
+  *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv));
 }
 
 // ---- fp32 path: one wave per (b, node, query head), keys in sequence ----
@@ -644,7 +657,7 @@ Plan make_plan(int B, int Hq, int Hkv, int ctx_max, int T, int W) {
   if (p.NS < 1) p.NS = 1;
   if (p.NS > 1) {
     const size_t rows = static_cast<size_t>(p.NS) * B * Hkv * p.QRpad;
-    p.off_ml = round_up(rows * D * 4, 256);
+    p.off_ml = round_up(rows * D * 2, 256);
     p.ws_bytes = p.off_ml + round_up(rows * 2 * 4, 256);
   }
   return p;
@@ -751,7 +764,7 @@ extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const v
   a.out = static_cast<uint16_t*>(out);
   if (p.NS > 1) {
     char* w = static_cast<char*>(ws);
-    a.part_o = reinterpret_cast<float*>(w);
+    a.part_o = reinterpret_cast<uint16_t*>(w);
     a.part_ml = reinterpret_cast<float*>(w + p.off_ml);
   }
   a.lds_mask = p.lds_mask;
@@ -764,6 +777,6 @@ extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const v
   }
   if (rc || p.NS == 1) return rc;
   const int64_t rows = static_cast<int64_t>(B) * Hkv * p.QR;
-  hipLaunchKernelGGL(merge_splits, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(merge_splits, dim3(static_cast<unsigned>((rows + 7) / 8)), dim3(256), 0, stream, a);
   return check_launch("tree attention split merge");
 }

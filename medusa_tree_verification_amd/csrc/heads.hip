@@ -7,17 +7,19 @@
 // "skinny" product Y[n][r] = sum_k W[r][k] X[n][k] whose cost is reading W
 // from HBM once.
 //
-// bf16 design (gfx950): one wave owns 16 consecutive weight rows and streams
-// them along k in 128-byte-per-lane chunks (lane l reads row l%16 at k-slice
-// (l/16)*64 .. +64, so every wave load instruction covers 16 rows x 512
-// contiguous bytes).  The products run on v_mfma_f32_16x16x32_bf16 with the
-// weights as the A operand (16 rows) and the activation rows as B (up to 16
-// columns per tile, zero-padded).  The k order inside a chunk is permuted
-// identically for A and B, which leaves the dot products unchanged and lets
-// each lane consume its contiguous 128 bytes as 8 MFMA k-steps.  Two chunks
-// are kept in flight per wave (register double buffer).  The MFMA work is
-// far below the matrix-core peak; the point is that it costs almost no VALU
-// issue slots, so the wave spends its time keeping loads in flight.
+// bf16 design (gfx950): one workgroup owns 16 consecutive weight rows; its 4
+// waves split the k range (wave w streams chunks w, w+4, ...) and add their
+// partial sums through LDS in wave order at the end (deterministic).  A chunk
+// is 8 (one column tile) or 4 MFMA k-steps of 32 elements: lane l (row l%16,
+// group q = l/16) loads the 8 elements at 8q + 32j of k-step j, so one load
+// instruction covers 64 contiguous bytes of each of the 16 rows and the
+// lane's elements sit exactly in the k-slots v_mfma_f32_16x16x32_bf16 wants
+// (weights as the A operand, activation rows as B, up to 16 columns per tile,
+// zero-padded).  The activation rows are staged once per workgroup in LDS
+// when they fit, so the vector memory pipe carries only weights.  Two chunks
+// are kept in flight per wave (register double buffer).  The MFMA work is far
+// below the matrix-core peak; the point is that it costs almost no VALU issue
+// slots, so the waves spend their time keeping loads in flight.
 #include "internal.h"
 
 using namespace medusa;
@@ -26,6 +28,8 @@ using namespace medusa::dev;
 namespace {
 
 enum { EPI_RESID = 1, EPI_LOGITS = 2 };
+
+__host__ __device__ constexpr int round_up16(int x) { return (x + 15) & ~15; }
 
 struct GemmArgs {
   const uint16_t* W;  // group g: W + g*w_gstride, [R][Kd]
@@ -48,13 +52,15 @@ struct Chunk {
   uint4 v[CH];
 };
 
+// piece j of a lane's chunk: 8 elements at p + 32*j (lane group q = l/16 starts
+// at 8q, so one load instruction covers 64 contiguous bytes of each of the 16
+// rows); avail = elements of the row from p onward
 template <int CH>
 __device__ __forceinline__ void load_chunk(Chunk<CH>& c, const uint16_t* p, int avail) {
-  // avail: elements of this lane's slice that lie inside the row (>= 8*CH means all)
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
-    if (8 * j + 8 <= avail)
-      c.v[j] = *reinterpret_cast<const uint4*>(p + 8 * j);
+    if (32 * j + 8 <= avail)
+      c.v[j] = *reinterpret_cast<const uint4*>(p + 32 * j);
     else
       c.v[j] = make_uint4(0, 0, 0, 0);
   }
@@ -72,28 +78,42 @@ __device__ __forceinline__ void mfma_chunk(f32x4 (&acc)[NT], const Chunk<CH>& w,
   }
 }
 
-// grid: (ceil(R/64), G, passes); block: 256 (4 waves x 16 rows)
-template <int NT, int EPI>
+constexpr int XPAD = 8;              // LDS row padding of the staged activations (elements)
+constexpr int XLDS_MAX = 64 * 1024;  // largest activation block staged in LDS (more costs occupancy)
+
+// grid: (ceil(R/16), G, passes); block: 256 (4 waves on the same 16 rows)
+template <int NT, int EPI, bool XLDS>
 __global__ __launch_bounds__(256) void skinny_gemm_bf16(GemmArgs a) {
-  constexpr int CH = (NT == 1) ? 8 : 4;  // 16-byte loads per lane per chunk
-  constexpr int SLICE = 8 * CH;          // elements per lane per chunk
-  constexpr int STEP = 4 * SLICE;        // elements per chunk (4 lane groups)
+  constexpr int CH = (NT == 1) ? 8 : 4;  // MFMA k-steps (16-byte loads per lane) per chunk
+  constexpr int STEP = 32 * CH;          // elements per chunk
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = blockIdx.y;
   const int n0 = blockIdx.z * NT * 16;
-  const int row0 = blockIdx.x * 64 + wave * 16;
-  if (row0 >= a.R) return;  // no block-level synchronisation in this kernel
+  const int row0 = blockIdx.x * 16;
+  const int nl = min(NT * 16, a.N - n0);  // activation rows of this pass
   const int rl = min(row0 + (lane & 15), a.R - 1);
-  const int kq = (lane >> 4) * SLICE;
+  const int kq = (lane >> 4) * 8;
   const uint16_t* wp = a.W + g * a.w_gstride + static_cast<int64_t>(rl) * a.Kd + kq;
-  const uint16_t* xp[NT];
-  bool xv[NT];
+  const uint16_t* xg = a.X + g * a.x_gstride + static_cast<int64_t>(n0) * a.Kd;
+  const int xrow = a.Kd + XPAD;
+  uint16_t* sx = reinterpret_cast<uint16_t*>(smem);
+  if constexpr (XLDS) {
+    // stage the activation rows n0 .. n0+nl-1 (16-byte pieces, Kd % 8 == 0)
+    const int pieces = nl * (a.Kd / 8);
+    for (int i = threadIdx.x; i < pieces; i += 256) {
+      const int n = i / (a.Kd / 8), k = (i % (a.Kd / 8)) * 8;
+      *reinterpret_cast<uint4*>(sx + n * xrow + k) =
+          *reinterpret_cast<const uint4*>(xg + static_cast<int64_t>(n) * a.Kd + k);
+    }
+    __syncthreads();
+  }
+  int xo[NT];  // this lane's activation row (offset), -1 beyond N
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    int n = n0 + t * 16 + (lane & 15);
-    xv[t] = n < a.N;
-    xp[t] = a.X + g * a.x_gstride + static_cast<int64_t>(xv[t] ? n : 0) * a.Kd + kq;
+    const int n = t * 16 + (lane & 15);
+    xo[t] = n < nl ? (XLDS ? n * xrow : n * a.Kd) + kq : -1;
   }
   f32x4 acc[NT];
 #pragma unroll
@@ -101,22 +121,47 @@ __global__ __launch_bounds__(256) void skinny_gemm_bf16(GemmArgs a) {
 
   const int nchunks = (a.Kd + STEP - 1) / STEP;
   Chunk<CH> wa, wb, xa[NT], xb[NT];
-  auto load = [&](Chunk<CH>& w, Chunk<CH>(&x)[NT], int c) {
-    int avail = a.Kd - c * STEP - kq;
+  auto load = [&](Chunk<CH>& w, Chunk<CH>(&x)[NT], int c) __attribute__((always_inline)) {
+    const int avail = a.Kd - c * STEP - kq;
     load_chunk<CH>(w, wp + static_cast<int64_t>(c) * STEP, avail);
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      load_chunk<CH>(x[t], xp[t] + static_cast<int64_t>(c) * STEP, xv[t] ? avail : 0);
+    for (int t = 0; t < NT; ++t) {
+      if (xo[t] < 0) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) x[t].v[j] = make_uint4(0, 0, 0, 0);
+      } else if constexpr (XLDS) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          x[t].v[j] = (32 * j + 8 <= avail) ? *reinterpret_cast<const uint4*>(sx + xo[t] + c * STEP + 32 * j)
+                                            : make_uint4(0, 0, 0, 0);
+      } else {
+        load_chunk<CH>(x[t], xg + xo[t] + static_cast<int64_t>(c) * STEP, avail);
+      }
+    }
   };
-  load(wa, xa, 0);
-  int c = 0;
-  for (; c + 2 <= nchunks; c += 2) {
-    load(wb, xb, c + 1);
+  // this wave's chunks: wave, wave + 4, ...
+  int c = wave;
+  if (c < nchunks) load(wa, xa, c);
+  for (; c + 4 < nchunks; c += 8) {
+    load(wb, xb, c + 4);
     mfma_chunk<NT, CH>(acc, wa, xa);
-    if (c + 2 < nchunks) load(wa, xa, c + 2);
+    if (c + 8 < nchunks) load(wa, xa, c + 8);
     mfma_chunk<NT, CH>(acc, wb, xb);
   }
   if (c < nchunks) mfma_chunk<NT, CH>(acc, wa, xa);
+
+  // waves 1-3 hand their partial sums to wave 0 (added in wave order)
+  f32x4* red = reinterpret_cast<f32x4*>(smem + (XLDS ? round_up16(nl * xrow * 2) : 0));
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[((wave - 1) * NT + t) * 64 + lane] = acc[t];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] += red[(w * NT + t) * 64 + lane];
 
   // C layout: lane holds column (lane & 15) and rows 4*(lane >> 4) + e
   const int rbase = row0 + 4 * (lane >> 4);
@@ -207,18 +252,43 @@ __global__ __launch_bounds__(256) void gemv_f32(GemvF32Args a) {
   }
 }
 
+template <int NT, int EPI>
+int launch_nt(const GemmArgs& a, int G, hipStream_t s) {
+  const dim3 grid((a.R + 15) / 16, G, (a.N + NT * 16 - 1) / (NT * 16));
+  const int nl = a.N < NT * 16 ? a.N : NT * 16;
+  const int xbytes = static_cast<int>(round_up(static_cast<size_t>(nl) * (a.Kd + XPAD) * 2, 16));
+  const int red = 3 * NT * 64 * 16;
+  if (xbytes <= XLDS_MAX) {
+    const int lds = xbytes + red;
+    if (lds > 64 * 1024) {
+      static int allowed = 0;
+      if (lds > allowed) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_gemm_bf16<NT, EPI, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
+          (void)hipGetLastError();
+          set_error("cannot allow %d bytes of dynamic LDS for the heads GEMM", lds);
+          return MEDUSA_EUNSUPPORTED;
+        }
+        allowed = lds;
+      }
+    }
+    hipLaunchKernelGGL((skinny_gemm_bf16<NT, EPI, true>), grid, dim3(256), lds, s, a);
+  } else {
+    hipLaunchKernelGGL((skinny_gemm_bf16<NT, EPI, false>), grid, dim3(256), red, s, a);
+  }
+  return check_launch(EPI == EPI_RESID ? "heads residual block (bf16)" : "heads vocab projection (bf16)");
+}
+
 template <int EPI>
 int launch_bf16(const GemmArgs& a, int G, hipStream_t s) {
   int nt = (a.N + 15) / 16;
   if (nt > 4) nt = 4;
-  dim3 grid((a.R + 63) / 64, G, (a.N + nt * 16 - 1) / (nt * 16));
   switch (nt) {
-    case 1: hipLaunchKernelGGL((skinny_gemm_bf16<1, EPI>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((skinny_gemm_bf16<2, EPI>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((skinny_gemm_bf16<3, EPI>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((skinny_gemm_bf16<4, EPI>), grid, dim3(256), 0, s, a); break;
+    case 1: return launch_nt<1, EPI>(a, G, s);
+    case 2: return launch_nt<2, EPI>(a, G, s);
+    case 3: return launch_nt<3, EPI>(a, G, s);
+    default: return launch_nt<4, EPI>(a, G, s);
   }
-  return check_launch(EPI == EPI_RESID ? "heads residual block (bf16)" : "heads vocab projection (bf16)");
 }
 
 template <int EPI>
