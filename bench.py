@@ -39,11 +39,46 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=32,
                    help="attention layers the CPU oracle runs (scaled to all layers)")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="run only a plain device copy of MIB MiB (4 times) and exit: the "
+                        "calibration run for HBM byte counters")
     return p.parse_args()
+
+
+def copy_probe(mib: int) -> None:
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) of a profiler run."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(4):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "repeats": 4}), flush=True)
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def counter_traffic(w, label: str, source: str):
+    """HBM bytes per launch measured by the FETCH_SIZE / WRITE_SIZE counter runs
+    recorded in profiles/hbm_counters_<workload>.txt (scaled by a plain copy
+    of known size), or None when there is no record for this workload or the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{w.name}.txt")
+    try:
+        with open(path) as f:
+            rec = [json.loads(l[len("record: "):]) for l in f if l.startswith("record: ")][-1]
+        with open(os.path.join(ROOT, "medusa_tree_verification_amd", "csrc", source), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("sources", {}).get(source) != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch", {}).get(label)
 
 
 def attention_bytes(w) -> int:
@@ -263,6 +298,9 @@ def cpu_baseline(w, n_layers, min_seconds=10.0, max_steps=40):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path's multi-GPU "
               "sharding is described in DESIGN.md but not built", file=sys.stderr)
@@ -283,12 +321,14 @@ def main():
     if dominant_attention:
         roof = {"kernel": "tree attention, one layer (tree_attn_bf16 + merge_splits)", "bound": "hbm",
                 "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                "traffic": counter_traffic(w, "tree_attention", "attention.hip"),
                 "bytes_per_launch": a_bytes, "us_per_launch": round(attn_us, 2)}
     else:
         roof = {"kernel": "skinny_gemm_bf16 x2 (residual block + vocab projection)", "bound": "hbm",
                 "achieved": round(heads_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(heads_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(heads_gbs / HBM_PEAK_GBS, 4),
+                "traffic": counter_traffic(w, "heads", "heads.hip"),
                 "bytes_per_launch": h_bytes, "us_per_launch": round(stages_us["heads"], 2)}
     result = {
         "metric": METRIC,
