@@ -7,21 +7,20 @@
 // depth d, so node n carries candidate rank(n) of head depth(n), and sits
 // depth(n) positions after the cached context.
 //
-// Order: larger logit first; equal logits by smaller index.  Comparing
-// (value, index) pairs this way is a total order, so the result is unique
-// and bit-exact.
+// Order: larger logit first; equal logits by smaller index (-0 and +0 are
+// equal).  Comparing (value, index) pairs this way is a total order, so the
+// result is unique and bit-exact.
 //
-// One workgroup of 1024 threads per (head, sequence), three phases:
-//   1. every thread takes the best of its strided share of the row (kept in
-//      registers when the row has at most 32 values per thread);
-//   2. the k-th best of the 1024 per-thread bests is a threshold: the k
-//      threads whose best beats or equals it hold k distinct entries at or
-//      above it, so every true top-k entry is at or above it too.  It is
-//      found by k wave arg-max rounds per wave, then k rounds over the
-//      waves' survivors;
-//   3. entries at or above the threshold (at most k per contributing thread,
-//      i.e. at most k * values-per-thread) are collected in LDS and the exact
-//      top-k is selected from them by k more arg-max rounds.
+// One workgroup of 1024 threads per (head, sequence), radix select:
+//   1. each logit becomes an order-preserving 32-bit key (larger logit ->
+//      larger key; -0 is keyed as +0);
+//   2. the k-th largest key K* is found digit by digit (11, 11 and 10 bits):
+//      an LDS histogram of the keys that match the digits found so far, then
+//      a scan from the top bucket down finds the bucket holding the k-th;
+//   3. every key above K* is a winner; when more keys equal K* than are still
+//      needed, the smallest indices among them are found the same way (a
+//      radix select on the index);
+//   4. the k winners are ranked by (value, index) inside one wave.
 // The same workgroup then writes the tree tokens and positions of the nodes
 // at depth head+1 (and the root, for head 0).
 #include "internal.h"
@@ -32,25 +31,12 @@ namespace {
 
 constexpr int THREADS = 1024;
 constexpr int WAVES = THREADS / 64;
-constexpr int REG_VALUES = 32;            // values per thread kept in registers
-constexpr int MAX_CAND = 4096;            // LDS candidate capacity
-constexpr unsigned NONE = 0xffffffffu;    // index of an empty / removed slot
+constexpr int REG_VALUES = 32;  // values per thread kept in registers
+constexpr int BINS = 2048;      // histogram buckets (11-bit digits)
 
-// (v, i) beats (w, j) in the output order
-__device__ __forceinline__ bool beats(float v, unsigned i, float w, unsigned j) {
-  return v > w || (v == w && i < j);
-}
-
-__device__ __forceinline__ void wave_argmax(float& v, unsigned& i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off, 64);
-    const unsigned oi = __shfl_xor(i, off, 64);
-    if (beats(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
+__device__ __forceinline__ uint32_t order_key(float y) {
+  uint32_t u = __float_as_uint(y == 0.f ? 0.f : y);  // -0 keyed as +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 struct CandArgs {
@@ -66,45 +52,47 @@ struct CandArgs {
   int32_t* pos;          // [B][T]
 };
 
-// k rounds of wave arg-max over per-lane slot arrays (slots kept in LDS).
-// cv/ci: the lane's slots are cand_v[base + lane + 64*s], s < per_lane.
-// Returns in lanes r < kd the r-th best (value, index); removes winners.
-__device__ void wave_select(float* cand_v, unsigned* cand_i, int n, int kd, float& out_v,
-                            unsigned& out_i) {
-  const int lane = threadIdx.x & 63;
-  // lane-local best slot
-  auto local_best = [&](float& bv, unsigned& bi, int& bs) {
-    bv = -INFINITY;
-    bi = NONE;
-    bs = -1;
-    for (int s = lane; s < n; s += 64) {
-      if (beats(cand_v[s], cand_i[s], bv, bi)) {
-        bv = cand_v[s];
-        bi = cand_i[s];
-        bs = s;
-      }
-    }
-  };
-  float bv;
-  unsigned bi;
-  int bs;
-  local_best(bv, bi, bs);
-  out_v = -INFINITY;
-  out_i = NONE;
-  for (int r = 0; r < kd; ++r) {
-    float wv = bv;
-    unsigned wi = bi;
-    wave_argmax(wv, wi);
-    if (lane == r) {
-      out_v = wv;
-      out_i = wi;
-    }
-    if (wi != NONE && bi == wi) {  // owner removes the winner and rescans its slots
-      cand_v[bs] = -INFINITY;
-      cand_i[bs] = NONE;
-      local_best(bv, bi, bs);
+struct Shared {
+  int hist[BINS];
+  int wave_sum[WAVES];
+  int found_bin, found_before;  // bucket of the target rank, count above it
+  int n_win;
+  uint32_t win_key[MEDUSA_MAX_TOPK];
+  uint32_t win_idx[MEDUSA_MAX_TOPK];
+  int top[MEDUSA_MAX_TOPK];
+};
+
+// Given the histogram of one digit, find the bucket that holds the element
+// of rank `want` (1-based) counting from the top bucket (descending = true)
+// or from the bottom one.  Writes found_bin / found_before.
+__device__ void find_bucket(Shared& sh, int want, bool descending) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // thread t owns ordered positions 2t and 2t+1
+  const int b0 = descending ? BINS - 1 - 2 * tid : 2 * tid;
+  const int b1 = descending ? b0 - 1 : b0 + 1;
+  const int h0 = sh.hist[b0], h1 = sh.hist[b1];
+  int x = h0 + h1;  // inclusive scan over threads in position order
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh.wave_sum[wave] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += sh.wave_sum[w];
+  const int incl = before + x;
+  const int excl = incl - h0 - h1;
+  if (excl < want && want <= incl) {
+    if (want <= excl + h0) {
+      sh.found_bin = b0;
+      sh.found_before = excl;
+    } else {
+      sh.found_bin = b1;
+      sh.found_before = excl + h0;
     }
   }
+  __syncthreads();
 }
 
 template <bool REG>
@@ -112,116 +100,103 @@ __global__ __launch_bounds__(THREADS) void topk_tree_kernel(CandArgs a) {
   const int head = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const float* x = a.logits + (static_cast<int64_t>(b) * a.K + head) * a.V;
   const int kd = a.kpd[head];
+  __shared__ Shared sh;
 
-  __shared__ float s_v[MAX_CAND];
-  __shared__ unsigned s_i[MAX_CAND];
-  __shared__ int s_n;
-  __shared__ float s_thv;
-  __shared__ unsigned s_thi;
-  __shared__ int s_top[MEDUSA_MAX_TOPK];
-
-  // ---- 1. per-thread best ----
-  float vals[REG ? REG_VALUES : 1];
-  float bv = -INFINITY;
-  unsigned bi = NONE;
+  // ---- 1. keys ----
+  uint32_t keys[REG ? REG_VALUES : 1];
   if (REG) {
 #pragma unroll
     for (int j = 0; j < REG_VALUES; ++j) {
       const int v = tid + j * THREADS;
-      vals[j] = v < a.V ? x[v] : -INFINITY;
+      keys[j] = v < a.V ? order_key(x[v]) : 0u;  // key 0 is below every logit's key
     }
+  }
+  // visit every (key, index) of the row (registers or a strided re-read)
+  auto for_each = [&](auto&& f) __attribute__((always_inline)) {
+    if (REG) {
 #pragma unroll
-    for (int j = 0; j < REG_VALUES; ++j) {
-      const unsigned v = tid + j * THREADS;
-      if (v < static_cast<unsigned>(a.V) && beats(vals[j], v, bv, bi)) {
-        bv = vals[j];
-        bi = v;
+      for (int j = 0; j < REG_VALUES; ++j) {
+        const int v = tid + j * THREADS;
+        if (v < a.V) f(keys[j], static_cast<uint32_t>(v));
       }
-    }
-  } else {
-    for (int v = tid; v < a.V; v += THREADS) {
-      const float y = x[v];
-      if (beats(y, v, bv, bi)) {
-        bv = y;
-        bi = v;
-      }
-    }
-  }
-
-  // ---- 2. threshold = k-th best of the per-thread bests ----
-  {
-    float cv = bv;
-    unsigned ci = bi;
-    float keep_v = -INFINITY;
-    unsigned keep_i = NONE;
-    for (int r = 0; r < kd; ++r) {  // wave-level: one slot per lane
-      float wv = cv;
-      unsigned wi = ci;
-      wave_argmax(wv, wi);
-      if (lane == r) {
-        keep_v = wv;
-        keep_i = wi;
-      }
-      if (wi != NONE && ci == wi) {
-        cv = -INFINITY;
-        ci = NONE;
-      }
-    }
-    if (lane < kd) {
-      s_v[wave * kd + lane] = keep_v;
-      s_i[wave * kd + lane] = keep_i;
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    float ov;
-    unsigned oi;
-    wave_select(s_v, s_i, WAVES * kd, kd, ov, oi);
-    if (lane == kd - 1) {
-      s_thv = ov;
-      s_thi = oi;
-    }
-    if (lane == 0) s_n = 0;
-  }
-  __syncthreads();
-  const float thv = s_thv;
-  const unsigned thi = s_thi;
-
-  // ---- 3. collect entries at or above the threshold, select exactly ----
-  auto offer = [&](float y, unsigned v) {
-    if (v == thi || beats(y, v, thv, thi)) {
-      const int slot = atomicAdd(&s_n, 1);
-      if (slot < MAX_CAND) {
-        s_v[slot] = y;
-        s_i[slot] = v;
-      }
+    } else {
+      for (int v = tid; v < a.V; v += THREADS) f(order_key(x[v]), static_cast<uint32_t>(v));
     }
   };
-  if (REG) {
-#pragma unroll
-    for (int j = 0; j < REG_VALUES; ++j) {
-      const unsigned v = tid + j * THREADS;
-      if (v < static_cast<unsigned>(a.V)) offer(vals[j], v);
-    }
-  } else {
-    for (int v = tid; v < a.V; v += THREADS) offer(x[v], v);
+
+  // ---- 2. K* = the kd-th largest key, one digit at a time ----
+  uint32_t prefix = 0, pmask = 0;
+  int want = kd;  // rank of K* among the keys matching the prefix
+  const int shifts[3] = {21, 10, 0};
+  const uint32_t widths[3] = {0x7FFu, 0x7FFu, 0x3FFu};
+  for (int p = 0; p < 3; ++p) {
+    for (int i = tid; i < BINS; i += THREADS) sh.hist[i] = 0;
+    __syncthreads();
+    for_each([&](uint32_t k, uint32_t) {
+      if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shifts[p]) & widths[p]], 1);
+    });
+    __syncthreads();
+    find_bucket(sh, want, true);
+    want -= sh.found_before;
+    prefix |= static_cast<uint32_t>(sh.found_bin) << shifts[p];
+    pmask |= widths[p] << shifts[p];
+    __syncthreads();  // everyone has read found_* before the next pass rewrites it
   }
+  const uint32_t kstar = prefix;
+  const int equal = sh.hist[kstar & 0x3FFu];  // keys equal to K* (last digit's bucket)
+  // keys above K*: kd - want of them; ties needed: want (1 <= want <= equal)
+
+  // ---- 3. winners: keys above K*, then the `want` smallest tied indices ----
+  uint32_t imax = 0xFFFFFFFFu;  // take tied indices <= imax
+  if (want < equal) {
+    // radix select of the want-th smallest index among keys == K* (2 digits)
+    uint32_t ip = 0, im = 0;
+    int w2 = want;
+    const int ishift[2] = {11, 0};
+    for (int p = 0; p < 2; ++p) {
+      __syncthreads();
+      for (int i = tid; i < BINS; i += THREADS) sh.hist[i] = 0;
+      __syncthreads();
+      for_each([&](uint32_t k, uint32_t v) {
+        if (k == kstar && (v & im) == ip) atomicAdd(&sh.hist[(v >> ishift[p]) & 0x7FFu], 1);
+      });
+      __syncthreads();
+      find_bucket(sh, w2, false);
+      w2 -= sh.found_before;
+      ip |= static_cast<uint32_t>(sh.found_bin) << ishift[p];
+      im |= 0x7FFu << ishift[p];
+    }
+    imax = ip;
+  }
+  if (tid == 0) sh.n_win = 0;
   __syncthreads();
-  if (wave == 0) {
-    const int n = min(s_n, MAX_CAND);
-    float ov;
-    unsigned oi;
-    wave_select(s_v, s_i, n, kd, ov, oi);
-    if (lane < kd) s_top[lane] = static_cast<int>(oi);
+  for_each([&](uint32_t k, uint32_t v) {
+    if (k > kstar || (k == kstar && v <= imax)) {
+      const int slot = atomicAdd(&sh.n_win, 1);
+      if (slot < MEDUSA_MAX_TOPK) {
+        sh.win_key[slot] = k;
+        sh.win_idx[slot] = v;
+      }
+    }
+  });
+  __syncthreads();
+
+  // ---- 4. rank the kd winners by (value desc, index asc) ----
+  if (tid < kd) {
+    const uint32_t k = sh.win_key[tid], v = sh.win_idx[tid];
+    int r = 0;
+    for (int j = 0; j < kd; ++j) {
+      const uint32_t kj = sh.win_key[j], vj = sh.win_idx[j];
+      r += (kj > k || (kj == k && vj < v)) ? 1 : 0;
+    }
+    sh.top[r] = static_cast<int>(v);
   }
   __syncthreads();
 
   int32_t* out = a.topk + (static_cast<int64_t>(b) * a.K + head) * a.kmax;
-  for (int j = tid; j < a.kmax; j += THREADS) out[j] = j < kd ? s_top[j] : -1;
+  for (int j = tid; j < a.kmax; j += THREADS) out[j] = j < kd ? sh.top[j] : -1;
 
   // tree tokens of the nodes this head feeds
   const int c = a.ctx[b];
@@ -233,7 +208,7 @@ __global__ __launch_bounds__(THREADS) void topk_tree_kernel(CandArgs a) {
         a.pos[static_cast<int64_t>(b) * a.T] = c;
       }
     } else if (d == head + 1) {
-      a.tree_tokens[static_cast<int64_t>(b) * a.T + n] = s_top[a.rank[n]];
+      a.tree_tokens[static_cast<int64_t>(b) * a.T + n] = sh.top[a.rank[n]];
       a.pos[static_cast<int64_t>(b) * a.T + n] = c + d;
     }
   }
@@ -254,12 +229,8 @@ extern "C" int medusa_tree_candidates(const float* head_logits, const int32_t* r
   for (int d = 0; d < tree->K; ++d)
     MEDUSA_CHECK_ARG(tree->kpd[d] <= V, "head %d keeps %d candidates but V=%d", d + 1,
                      tree->kpd[d], V);
-  // the candidate list holds at most k * ceil(V / 1024) entries
-  const long long per_thread = (static_cast<long long>(V) + THREADS - 1) / THREADS;
-  if (per_thread * tree->kmax > MAX_CAND) {
-    set_error("top-%d over V=%d exceeds the candidate buffer (%d)", tree->kmax, V, MAX_CAND);
-    return MEDUSA_EUNSUPPORTED;
-  }
+  // indices are radix-selected in two 11-bit digits
+  MEDUSA_CHECK_ARG(V <= (1 << 22), "V=%d above 4194304", V);
   CandArgs a{};
   a.logits = head_logits;
   a.K = tree->K;

@@ -79,3 +79,22 @@ def test_candidates_deterministic():
     b = api.tree_candidates(logits, r, r, t)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("V", [40000, 131072])
+def test_candidates_large_vocab(V):
+    """Vocabularies past 32768 entries re-read the row on every pass."""
+    kpd = (10, 5)
+    parent, rank = synth.cartesian_tree(kpd)
+    g = torch.Generator(device=DEV).manual_seed(V)
+    logits = torch.randn((2, 2, V), generator=g, device=DEV)
+    logits[1, 1, V // 2:] = logits[1, 1, : V - V // 2].round()  # ties among the largest values
+    _run_and_compare(logits, parent, rank, kpd, [5, 6], [0, 9])
+
+
+def test_candidates_all_equal():
+    """Every logit equal: the k lowest indices, in index order."""
+    kpd = (10, 10, 5)
+    parent, rank = synth.cost_ordered_tree(kpd, 40)
+    logits = torch.full((1, 3, 32000), 0.5, device=DEV)
+    _run_and_compare(logits, parent, rank, kpd, [3], [8])
