@@ -8,7 +8,10 @@ inputs are resident in HBM before timing starts.  The step is captured once
 as a HIP graph and replayed (the host never sits in the timed loop).  For the
 per-stage and per-kernel figures every stage is captured as a graph of its
 own and replayed between HIP events on the launch stream; the attention
-stage's graph holds all layers, so its time / L is one layer's launch.
+stage's graph holds all layers, so its time / L is one layer's launch.  The
+commit of the accepted path (medusa_commit_accepted, KV rollback over all
+layers) closes a step in a decoding loop; it is timed as a stage of its own
+and reported beside the step, not inside it.
 
 Prints one JSON line (see the keys at the end of main()).
 """
@@ -111,7 +114,20 @@ def build_step(w, dev):
     tree = api.Tree(parent, rank, w.topk)
     root = synth.roots(w, dev)
     ctx = torch.full((w.B,), w.ctx, dtype=torch.int32, device=dev)
-    layers = [synth.attention_inputs(w, l, dev)[:3] for l in range(w.L)]
+    # every layer's K/V in one [L][B][Hkv][S_cap][D] pair (own buffers per
+    # layer, uniform layer stride for the commit)
+    q0, k0, v0 = synth.attention_inputs(w, 0, dev)[:3]
+    k_all = torch.empty((w.L,) + tuple(k0.shape), dtype=k0.dtype, device=dev)
+    v_all = torch.empty_like(k_all)
+    qs = [q0]
+    k_all[0], v_all[0] = k0, v0
+    del k0, v0
+    for l in range(1, w.L):
+        q, k, v = synth.attention_inputs(w, l, dev)[:3]
+        qs.append(q)
+        k_all[l], v_all[l] = k, v
+        del k, v
+    layers = [(qs[l], k_all[l], v_all[l]) for l in range(w.L)]
     base = synth.normal((w.B, w.T, w.V), w.base_logit_std, synth.seed_for(w.cfg_id, synth.T_BASE), dev)
     ua = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_UACC), dev)
     us = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_USMP), dev)
@@ -147,6 +163,13 @@ def build_step(w, dev):
         for tau, o in acc_outs.items():
             api.accept_paths(base, logits, toks, tree, ua, us, tau, outs=o, ws=ws_acc)
 
+    ctx_next = torch.empty_like(ctx)
+    root_next = torch.empty_like(root)
+    acc0 = acc_outs[w.temperature[0]]
+
+    def stage_commit():  # after the step: KV rollback / compaction of the accepted path
+        api.commit_accepted(k_all, v_all, acc0[0], acc0[2], acc0[1], ctx, tree, ctx_next, root_next)
+
     def step():
         stage_heads()
         stage_candidates()
@@ -155,7 +178,7 @@ def build_step(w, dev):
         stage_accept()
 
     keep = dict(hidden=hidden, w1=w1, wlm=wlm, tree=tree, layers=layers, base=base)
-    return step, (stage_heads, stage_candidates, stage_attention, stage_accept), keep
+    return step, (stage_heads, stage_candidates, stage_attention, stage_accept, stage_commit), keep
 
 
 def _capture(fn):
@@ -198,7 +221,7 @@ def time_gpu(w, args):
     torch.cuda.set_device(dev)
     step, stages, keep = build_step(w, dev)
     torch.cuda.synchronize()
-    stage_heads, stage_candidates, stage_attention, stage_accept = stages
+    stage_heads, stage_candidates, stage_attention, stage_accept, stage_commit = stages
 
     run = step if args.eager else _capture(step).replay
     log(f"warmup {args.warmup}, timing {args.steps} steps ({'eager' if args.eager else 'graph'})")
@@ -223,7 +246,8 @@ def time_gpu(w, args):
             stage_attention(l)
 
     graphs = {"heads": _capture(stage_heads), "candidates": _capture(stage_candidates),
-              "attention": _capture(all_layers), "accept": _capture(stage_accept)}
+              "attention": _capture(all_layers), "accept": _capture(stage_accept),
+              "commit": _capture(stage_commit)}
     reps = max(5, args.steps)
     stages_us = {n: 1000.0 * _time_replays(g.replay, reps, 3) for n, g in graphs.items()}
     attn_call_us = stages_us["attention"] / w.L

@@ -8,6 +8,9 @@
  *   medusa_tree_attention   tree-masked attention of one layer (split-KV)
  *   medusa_accept_paths     longest accepted root-to-leaf path (greedy or
  *                           rejection sampling)
+ * and one call closes the step:
+ *   medusa_commit_accepted  KV rollback / compaction of the accepted path,
+ *                           next root and context length
  *
  * Pages that define the operations (cited per call):
  *   P1 "Medusa 심층 아키텍처: 별도 초안 모델을 제거한 다중 헤드(Multi-Head) 추측 디코딩과
@@ -245,6 +248,39 @@ int medusa_accept_paths(const float* base_logits, const float* head_logits,
                         const float* u_accept, const float* u_sample, float temperature,
                         int B, int V, int32_t* accept_len, int32_t* out_tokens,
                         int32_t* out_nodes, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * After acceptance: commit the accepted path (KV rollback / compaction)
+ *
+ * P3, architecture section (the pipeline ends with rollback and the
+ * confirmed correction token) and section 5, Case 2 (K-token verification
+ * with early rejection and rollback); P4, section 1.3: the matched drafts
+ * are kept, everything after the first mismatch is discarded.  The tree
+ * tokens' K/V sit in slots ctx .. ctx+T-1 (node n at ctx + n).  For every
+ * layer, sequence and K/V head the K/V of the accepted node at depth d moves
+ * from slot ctx + out_nodes[b][d] to slot ctx + d, d = 1 .. accept_len[b]
+ * (the root stays at ctx); the other tree slots are simply abandoned.  The
+ * next step starts from
+ *   ctx_next[b]  = ctx_len[b] + accept_len[b] + 1
+ *   root_next[b] = out_tokens[b][accept_len[b]]   (correction or bonus token)
+ * whose K/V the next step computes at slot ctx_next[b].
+ *
+ *   k_cache, v_cache  layer l at base + l * layer_stride elements, each
+ *                     [B][Hkv][S_cap][D] dt (updated in place)
+ *   accept_len, out_nodes, out_tokens   as written by medusa_accept_paths
+ *   ctx_len [B] int32 (input); ctx_next, root_next [B] int32 (outputs, must
+ *           not alias ctx_len)
+ * Values outside their ranges are clamped (accept_len to 0..K, nodes to
+ * 0..T-1, ctx_len to 0..S_cap-T) so that no access leaves the caches; the
+ * caller keeps ctx_next + T <= S_cap for the next step.
+ * Constraints: D * element size a multiple of 16 bytes and at most 512;
+ * 16-byte aligned caches and layer stride.  No workspace.
+ * ------------------------------------------------------------------------ */
+int medusa_commit_accepted(void* k_cache, void* v_cache, int64_t layer_stride, int L,
+                           const int32_t* accept_len, const int32_t* out_nodes,
+                           const int32_t* out_tokens, const int32_t* ctx_len, int32_t* ctx_next,
+                           int32_t* root_next, const medusa_tree_t* tree, int B, int Hkv, int D,
+                           int S_cap, medusa_dtype_t dt, hipStream_t stream);
 
 #ifdef __cplusplus
 }

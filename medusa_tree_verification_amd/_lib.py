@@ -40,6 +40,9 @@ SIGNATURES = {
     "medusa_accept_paths": (c_int, [P_void, P_void, P_void, c_void_p, P_void, P_void, c_float,
                                     c_int, c_int, P_void, P_void, P_void, P_void, c_size_t,
                                     P_void]),
+    "medusa_commit_accepted": (c_int, [P_void, P_void, c_int64, c_int, P_void, P_void, P_void,
+                                       P_void, P_void, P_void, c_void_p, c_int, c_int, c_int,
+                                       c_int, c_int, P_void]),
 }
 
 _lib = None

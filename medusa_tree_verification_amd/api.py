@@ -207,3 +207,29 @@ def accept_paths(base_logits: torch.Tensor, head_logits: Optional[torch.Tensor],
                                    B, V, _ptr(acc), _ptr(toks), _ptr(nodes), _ptr(ws), nb,
                                    _stream(stream)))
     return acc, toks, nodes
+
+
+def commit_accepted(k_cache: torch.Tensor, v_cache: torch.Tensor, accept_len: torch.Tensor,
+                    out_nodes: torch.Tensor, out_tokens: torch.Tensor, ctx_len: torch.Tensor,
+                    tree: Tree, ctx_next=None, root_next=None, stream=None):
+    """k_cache/v_cache [L,B,Hkv,S_cap,D] or [B,Hkv,S_cap,D] (updated in place)
+    -> (ctx_next [B], root_next [B]) int32."""
+    lib = _lib.load()
+    if k_cache.dim() == 4:
+        L, (B, Hkv, S_cap, D) = 1, k_cache.shape
+        stride = B * Hkv * S_cap * D
+    else:
+        L, B, Hkv, S_cap, D = k_cache.shape
+        stride = k_cache.stride(0)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    dev = k_cache.device
+    if ctx_next is None:
+        ctx_next = torch.empty(B, dtype=torch.int32, device=dev)
+    if root_next is None:
+        root_next = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(lib.medusa_commit_accepted(_ptr(k_cache), _ptr(v_cache), stride, L, _ptr(accept_len),
+                                      _ptr(out_nodes), _ptr(out_tokens), _ptr(ctx_len),
+                                      _ptr(ctx_next), _ptr(root_next), tree.handle, B, Hkv, D,
+                                      S_cap, _dt(k_cache), _stream(stream)))
+    return ctx_next, root_next

@@ -296,3 +296,68 @@ def accept_inputs(w: Workload, parent: np.ndarray, tree_tokens: np.ndarray, devi
                 head[b, depths_of(parent)[c] - 1, int(tree_tokens[b, c])] += plant_boost * 0.5
                 u = c
     return (base.to(device), head.to(device), u_acc.to(device), u_smp.to(device))
+
+
+# ---------------------------------------------------------------------------
+# Toy target model for multi-step tests: a counter-based hash of the prefix.
+# SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+# generators", OOPSLA 2014) maps a 64-bit state to a 64-bit output; the
+# prefix hash folds every token in, and the logits of a prefix are the top
+# 24 bits of SplitMix64(hash ^ f(v)) scaled to [0, 1).  Host-only: the tests
+# feed its values to the device path and to the oracle alike.
+# ---------------------------------------------------------------------------
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(x: int) -> int:
+    x = (x + 0x9E3779B97F4A7C15) & _M64
+    z = x
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def _splitmix64_np(x: np.ndarray) -> np.ndarray:
+    x = x.astype(np.uint64) + np.uint64(0x9E3779B97F4A7C15)
+    z = x
+    z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+    z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def prefix_hash(tokens, seed: int = 0x51ED) -> int:
+    h = seed & _M64
+    for t in tokens:
+        h = splitmix64(h ^ (int(t) & _M64))
+    return h
+
+
+def toy_target_logits(h: int, V: int) -> np.ndarray:
+    """Logits [V] float32 in [0, 1) of the toy target after a prefix with hash h."""
+    with np.errstate(over="ignore"):
+        v = np.arange(V, dtype=np.uint64) * np.uint64(0x100000001B3) + np.uint64(1)
+        z = _splitmix64_np(np.uint64(h) ^ v)
+    return ((z >> np.uint64(40)).astype(np.float64) / float(1 << 24)).astype(np.float32)
+
+
+def toy_kv_rows(token: int, pos: int, layer: int, Hkv: int, D: int) -> np.ndarray:
+    """The toy model's K (or V) rows [Hkv][D] in [-1, 1) for a token at a
+    position: what a base-model forward would write into the cache."""
+    h = splitmix64(prefix_hash([token, pos, layer], seed=0xCAC4E))
+    with np.errstate(over="ignore"):
+        idx = np.arange(Hkv * D, dtype=np.uint64) * np.uint64(0x2545F4914F6CDD1D)
+        z = _splitmix64_np(np.uint64(h) ^ idx)
+    u = (z >> np.uint64(40)).astype(np.float64) / float(1 << 24)
+    return (2.0 * u - 1.0).astype(np.float32).reshape(Hkv, D)
+
+
+def toy_draft_logits(greedy_path, V: int, K: int, hit: np.ndarray, seed: int) -> np.ndarray:
+    """Head logits [K][V] for one step: N(0, 1) noise, plus +6 on the target's
+    greedy token at depth d+1 for the heads d with hit[d] true (drafts that
+    are right where hit says so)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((K, V)).astype(np.float32)
+    for d in range(K):
+        if hit[d]:
+            x[d, int(greedy_path[d])] += 6.0
+    return x

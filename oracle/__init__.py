@@ -23,6 +23,7 @@ Modules:
   attention  tree-masked attention, path-causal alternative    (P1, tree attention; P4 3.3)
   accept     greedy and rejection-sampling acceptance          (P1, rejection sampling; P3 2, 5; P4 1.3)
   step       the four stages composed
+  commit     KV rollback / compaction after acceptance; greedy decoding (P3 5; P4 1.3)
 
 Every function has at least one pin in ``tests/test_oracle_*.py`` that ties it
 to something other than itself (worked examples printed on the pages, closed

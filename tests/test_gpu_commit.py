@@ -1,0 +1,141 @@
+"""GPU parity of medusa_commit_accepted (KV rollback / compaction) against the
+oracle, and the multi-step greedy loop on the device: candidates -> tree
+attention -> greedy acceptance -> commit, step after step, must emit exactly
+the toy target's greedy decoding (P3, section 5) and leave exactly the
+committed sequence's K/V in the caches."""
+import numpy as np
+import pytest
+import torch
+
+from medusa_tree_verification_amd import api, synth
+from oracle import attention as oattn
+from oracle import commit as ocommit
+from oracle import tree as otree
+from helpers import TOL_BF16, announce, row_rel_err, to64
+from toy_model import ToyTarget, expected_cache_prefix, step_inputs, write_tree_kv
+from test_oracle_commit import run_oracle_loop
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("dtype,D,L", [(torch.bfloat16, 128, 3), (torch.float32, 64, 1), (torch.bfloat16, 256, 2)])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_commit_matches_oracle(dtype, D, L, seed):
+    rng = np.random.default_rng(seed)
+    kpd = [5, 4, 3, 2]
+    parent, rank = synth.random_tree(24, kpd, seed + 40)
+    t = api.Tree(parent, rank, kpd)
+    B, Hkv, T, K = 4, 3, len(parent), len(kpd)
+    ctx = [int(x) for x in rng.integers(0, 50, B)]
+    S_cap = max(ctx) + T + 3
+    k = torch.randn((L, B, Hkv, S_cap, D), dtype=torch.float32).to(dtype)
+    v = torch.randn((L, B, Hkv, S_cap, D), dtype=torch.float32).to(dtype)
+    kids = otree.children_in_rank_order(parent, rank)
+    acc, nodes, out = [], np.full((B, K + 1), -1), np.full((B, K + 1), -1)
+    for b in range(B):
+        path, u = [0], 0
+        while kids[u] and rng.random() < 0.85:
+            u = int(rng.choice(kids[u]))
+            path.append(u)
+        acc.append(len(path) - 1)
+        nodes[b, : len(path)] = path
+        out[b, : len(path)] = rng.integers(0, 1000, len(path))
+    ref_k, ref_v, ref_cn, ref_rn = ocommit.commit(k.float().numpy(), v.float().numpy(), ctx, acc, nodes, out)
+    kd, vd = k.to(DEV), v.to(DEV)
+    i32 = lambda x: torch.tensor(np.asarray(x), dtype=torch.int32, device=DEV)
+    announce("commit", dtype, D, L, seed)
+    cn, rn = api.commit_accepted(kd if L > 1 else kd[0], vd if L > 1 else vd[0], i32(acc), i32(nodes), i32(out),
+                                 i32(ctx), t)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kd.float().cpu().numpy(), ref_k)
+    np.testing.assert_array_equal(vd.float().cpu().numpy(), ref_v)
+    np.testing.assert_array_equal(cn.cpu().numpy(), ref_cn)
+    np.testing.assert_array_equal(rn.cpu().numpy(), ref_rn)
+
+
+def test_commit_argument_errors():
+    parent, rank = synth.cost_ordered_tree([3, 2], 6)
+    t = api.Tree(parent, rank, [3, 2])
+    z = torch.zeros(2, dtype=torch.int32, device=DEV)
+    zz = torch.zeros((2, 3), dtype=torch.int32, device=DEV)
+    k = torch.zeros((2, 1, 16, 4), dtype=torch.bfloat16, device=DEV)   # D * 2 bytes = 8: not a multiple of 16
+    with pytest.raises(api.MedusaError) as e:
+        api.commit_accepted(k, k.clone(), z, zz, zz, z, t)
+    assert e.value.code == api.EINVAL
+    k = torch.zeros((2, 1, 4, 128), dtype=torch.bfloat16, device=DEV)  # S_cap < T
+    with pytest.raises(api.MedusaError) as e:
+        api.commit_accepted(k, k.clone(), z, zz, zz, z, t)
+    assert e.value.code == api.EINVAL
+
+
+def test_multistep_greedy_loop_on_device():
+    """Ten steps for three sequences: every stage runs in the library; the
+    emitted tokens equal greedy decoding of the toy target and the oracle
+    loop's, the caches hold the committed sequence's K/V bit for bit, and
+    every step's tree attention over the evolving cache matches the oracle."""
+    target = ToyTarget(V=97)
+    kpd = [3, 2, 2]
+    parent, rank = synth.cost_ordered_tree(kpd, 12)
+    tree = api.Tree(parent, rank, kpd)
+    depth = otree.depth_of(parent)
+    vis = otree.visible_bruteforce(parent)
+    rng = np.random.default_rng(3)
+    prompts = [list(rng.integers(0, 97, n)) for n in (5, 1, 9)]
+    steps, B, K, T, L, Hkv, Hq, D = 10, 3, len(kpd), len(parent), 2, 2, 4, 128
+    S_cap = max(len(p) for p in prompts) + steps * (K + 1) + T + 1
+    kc = np.zeros((L, B, Hkv, S_cap, D), np.float32)
+    vc = np.zeros_like(kc)
+    for b, p in enumerate(prompts):
+        ek, ev = expected_cache_prefix(p, L, Hkv, D)
+        kc[:, b, :, : len(p)], vc[:, b, :, : len(p)] = ek, ev
+    k_dev = torch.from_numpy(kc).to(torch.bfloat16).to(DEV)
+    v_dev = torch.from_numpy(vc).to(torch.bfloat16).to(DEV)
+    committed = [list(p) for p in prompts]
+    roots = [int(np.argmax(target.logits(p))) for p in prompts]
+    emitted = [[r] for r in roots]
+    ctx_d = torch.tensor([len(p) for p in prompts], dtype=torch.int32, device=DEV)
+    root_d = torch.tensor(roots, dtype=torch.int32, device=DEV)
+    step_rng = np.random.default_rng(11)
+
+    def topk_on_device(heads):
+        _, toks, _ = api.tree_candidates(torch.from_numpy(heads).to(DEV), root_d, ctx_d, tree)
+        return toks.cpu().numpy()
+
+    for s in range(steps):
+        announce("loop step", s)
+        ctx = ctx_d.cpu().numpy()
+        _, toks, base = step_inputs(target, committed, roots, parent, depth, K, 0.7, step_rng, s, topk_on_device)
+        # the base model writes the tree tokens' K/V (host), then attends over them
+        kh = k_dev.float().cpu().numpy()
+        vh = v_dev.float().cpu().numpy()
+        write_tree_kv(kh, vh, ctx, toks, depth, L, Hkv, D)
+        k_dev.copy_(torch.from_numpy(kh).to(torch.bfloat16))
+        v_dev.copy_(torch.from_numpy(vh).to(torch.bfloat16))
+        q = torch.randn((B, T, Hq, D), generator=torch.Generator().manual_seed(s)).to(torch.bfloat16)
+        o = api.tree_attention(q.to(DEV), k_dev[0], v_dev[0], ctx_d, int(ctx.max()), tree)
+        ref = oattn.tree_attention(to64(q), to64(k_dev[0]), to64(v_dev[0]), ctx.tolist(), vis)
+        assert row_rel_err(to64(o), ref) <= TOL_BF16, s
+        acc, out_t, out_n = api.accept_paths(torch.from_numpy(base).to(DEV), None,
+                                             torch.from_numpy(toks.astype(np.int32)).to(DEV), tree, None, None, 0.0)
+        cn, rn = api.commit_accepted(k_dev, v_dev, acc, out_n, out_t, ctx_d, tree)
+        acc_h, out_h = acc.cpu().numpy(), out_t.cpu().numpy()
+        for b in range(B):
+            n = int(acc_h[b])
+            emitted[b] += [int(x) for x in out_h[b, : n + 1]]
+            committed[b] += [roots[b]] + [int(x) for x in out_h[b, :n]]
+        ctx_d, root_d = cn, rn
+        roots = [int(x) for x in rn.cpu().numpy()]
+    ref_emitted, _, _, ref_ctx, _ = run_oracle_loop(target, prompts, parent, rank, kpd, steps, 0.7, 11,
+                                                    L=L, Hkv=Hkv, D=D)
+    final_ctx = ctx_d.cpu().numpy()
+    kf, vf = k_dev.float().cpu().numpy(), v_dev.float().cpu().numpy()
+    for b, p in enumerate(prompts):
+        assert emitted[b] == target.greedy(p, len(emitted[b]))
+        assert emitted[b] == ref_emitted[b]
+        assert final_ctx[b] == len(committed[b]) == ref_ctx[b]
+        ek, ev = expected_cache_prefix(committed[b], L, Hkv, D)
+        ek = torch.from_numpy(ek).to(torch.bfloat16).float().numpy()
+        ev = torch.from_numpy(ev).to(torch.bfloat16).float().numpy()
+        np.testing.assert_array_equal(kf[:, b, :, : final_ctx[b]], ek)
+        np.testing.assert_array_equal(vf[:, b, :, : final_ctx[b]], ev)
