@@ -11,6 +11,9 @@
  * and one call closes the step:
  *   medusa_commit_accepted  KV rollback / compaction of the accepted path,
  *                           next root and context length
+ * and a host-only call chooses the static tree:
+ *   medusa_tree_optimize    the T-node tree that maximises expected accepted
+ *                           length under a per-depth, per-rank acceptance table
  *
  * Pages that define the operations (cited per call):
  *   P1 "Medusa 심층 아키텍처: 별도 초안 모델을 제거한 다중 헤드(Multi-Head) 추측 디코딩과
@@ -281,6 +284,28 @@ int medusa_commit_accepted(void* k_cache, void* v_cache, int64_t layer_stride, i
                            const int32_t* out_tokens, const int32_t* ctx_len, int32_t* ctx_next,
                            int32_t* root_next, const medusa_tree_t* tree, int B, int Hkv, int D,
                            int S_cap, medusa_dtype_t dt, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Static tree optimiser (host only)
+ *
+ * P2, paper-results section: an optimised tree configuration adds to the
+ * speed-up of tree attention; P1, tree-size trade-off section: the topology
+ * (usually 32-64 nodes) is chosen by profiling.  Given an acceptance table
+ * p[d][r] (probability that head d+1's rank-r candidate is the target's
+ * token, e.g. measured), a node (r_1..r_d) is accepted with probability
+ * prod_i p[i-1][r_i]; the returned tree holds the T - 1 most probable such
+ * tuples (ties: smaller depth, then the lexicographically smaller tuple),
+ * which maximises the expected accepted nodes per step, numbered
+ * breadth-first by (depth, tuple) so that it can be passed to
+ * medusa_tree_create directly.
+ *
+ *   p_accept     [K][kmax_in] row-major, values in [0, 1] (host)
+ *   k_per_depth  [K] candidates per head, 1..min(MEDUSA_MAX_TOPK, kmax_in)
+ *   parent_out, rank_out [T] int32 (host outputs)
+ *   expected_out expected accepted nodes per step (may be NULL)
+ * ------------------------------------------------------------------------ */
+int medusa_tree_optimize(const double* p_accept, int K, int kmax_in, const int32_t* k_per_depth,
+                         int T, int32_t* parent_out, int32_t* rank_out, double* expected_out);
 
 #ifdef __cplusplus
 }

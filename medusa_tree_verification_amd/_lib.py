@@ -43,6 +43,8 @@ SIGNATURES = {
     "medusa_commit_accepted": (c_int, [P_void, P_void, c_int64, c_int, P_void, P_void, P_void,
                                        P_void, P_void, P_void, c_void_p, c_int, c_int, c_int,
                                        c_int, c_int, P_void]),
+    "medusa_tree_optimize": (c_int, [ctypes.POINTER(ctypes.c_double), c_int, c_int, P_i32, c_int,
+                                     P_i32, P_i32, ctypes.POINTER(ctypes.c_double)]),
 }
 
 _lib = None

@@ -233,3 +233,18 @@ def commit_accepted(k_cache: torch.Tensor, v_cache: torch.Tensor, accept_len: to
                                       _ptr(ctx_next), _ptr(root_next), tree.handle, B, Hkv, D,
                                       S_cap, _dt(k_cache), _stream(stream)))
     return ctx_next, root_next
+
+
+def tree_optimize(p_accept, k_per_depth, T: int):
+    """Host-only: the T-node tree maximising expected accepted nodes under the
+    acceptance table p_accept [K][kmax] -> (parent, rank, expected)."""
+    lib = _lib.load()
+    p = np.ascontiguousarray(np.asarray(p_accept, dtype=np.float64))
+    kpd = _i32(k_per_depth)
+    K, kmax = p.shape
+    parent = np.zeros(T, np.int32)
+    rank = np.zeros(T, np.int32)
+    e = ctypes.c_double()
+    _check(lib.medusa_tree_optimize(p.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), K, kmax,
+                                    _p32(kpd), T, _p32(parent), _p32(rank), ctypes.byref(e)))
+    return parent, rank, e.value

@@ -361,3 +361,19 @@ def toy_draft_logits(greedy_path, V: int, K: int, hit: np.ndarray, seed: int) ->
         if hit[d]:
             x[d, int(greedy_path[d])] += 6.0
     return x
+
+
+def toy_draft_logits_ranked(greedy_path, V: int, ranks, seed: int) -> np.ndarray:
+    """Head logits [K][V]: N(0, 1) noise in which the target's greedy token at
+    depth d+1 sits exactly at rank ranks[d] (no placement when ranks[d] < 0)."""
+    rng = np.random.default_rng(seed)
+    K = len(ranks)
+    x = rng.standard_normal((K, V)).astype(np.float32)
+    for d in range(K):
+        r = int(ranks[d])
+        if r < 0:
+            continue
+        t = int(greedy_path[d])
+        others = np.sort(np.delete(x[d], t))[::-1]
+        x[d, t] = others[0] + 1.0 if r == 0 else 0.5 * (others[r - 1] + others[r])
+    return x

@@ -19,7 +19,8 @@ Pages cited (each function names the page and the section it follows):
 Modules:
   heads      residual SiLU block + vocab projection            (P1, heads)
   topk       per-head top-k                                    (P1, sketch code; P2, propose())
-  tree       static tree, ancestor sets, mask, tree tokens     (P1, tree attention; sketch code)
+  tree       static tree, ancestor sets, mask, tree tokens,    (P1, tree attention; sketch code;
+             expected accepted length, optimal tree (brute)     P2 paper results)
   attention  tree-masked attention, path-causal alternative    (P1, tree attention; P4 3.3)
   accept     greedy and rejection-sampling acceptance          (P1, rejection sampling; P3 2, 5; P4 1.3)
   step       the four stages composed

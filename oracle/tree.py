@@ -141,3 +141,41 @@ def depth_of(parent) -> np.ndarray:
     for n in range(1, T):
         d[n] = d[int(parent[n])] + 1
     return d
+
+
+def expected_accepted(parent, rank, p_accept) -> float:
+    """Expected accepted nodes per step of a static tree when the rank-r
+    candidate of head d is right with probability p_accept[d-1][r]
+    independently along a path (P2, paper-results section: an optimised
+    tree configuration; P1: topology chosen by profiling): the sum over
+    non-root nodes of the product of p along the root-to-node path."""
+    depth = depth_of(parent)
+    prob = [1.0] * len(parent)
+    total = 0.0
+    for n in range(1, len(parent)):
+        prob[n] = prob[int(parent[n])] * float(p_accept[depth[n] - 1][int(rank[n])])
+        total += prob[n]
+    return total
+
+
+def optimal_tree_bruteforce(p_accept, k_per_depth, T: int):
+    """Brute force over every prefix-closed set of T-1 rank tuples: the best
+    expected accepted nodes (tiny cases only)."""
+    import itertools
+    K = len(k_per_depth)
+    tuples = []
+    for d in range(1, K + 1):
+        tuples.extend(itertools.product(*[range(k) for k in k_per_depth[:d]]))
+    best = -1.0
+    for subset in itertools.combinations(tuples, T - 1):
+        s = set(subset)
+        if any(len(t) > 1 and t[:-1] not in s for t in s):
+            continue
+        val = 0.0
+        for t in s:
+            pr = 1.0
+            for d, r in enumerate(t):
+                pr *= float(p_accept[d][r])
+            val += pr
+        best = max(best, val)
+    return best

@@ -70,3 +70,53 @@ def expected_cache_prefix(seq, L, Hkv, D):
         for l in range(L):
             k[l, :, p] = synth.toy_kv_rows(int(t), p, l, Hkv, D)
     return k, -k
+
+
+class RankedDrafts:
+    """Draft heads whose right token lands at rank r with probability
+    hit[d] * (1 - q) * q^r (truncated at the head's k), else misses."""
+
+    def __init__(self, hit, q: float):
+        self.hit, self.q = list(hit), q
+
+    def ranks(self, rng, kpd):
+        out = []
+        for d, k in enumerate(kpd):
+            if rng.random() < self.hit[d]:
+                r = int(rng.geometric(1 - self.q)) - 1
+                out.append(r if r < k else -1)
+            else:
+                out.append(-1)
+        return out
+
+
+def simulate_accepts(target, drafts, parent, rank, kpd, steps, seed, prompt_len=4):
+    """Greedy Medusa with the oracle's stages on one sequence for `steps`
+    steps; returns the accepted length of every step and, per (depth, rank),
+    how often that candidate was tested (its parent accepted) and accepted."""
+    from oracle import accept as oaccept
+    from oracle import topk as otopk
+    from oracle import tree as otree
+    rng = np.random.default_rng(seed)
+    K, T = len(kpd), len(parent)
+    seq = list(rng.integers(0, target.V, prompt_len))
+    root = int(np.argmax(target.logits(seq)))
+    depth = otree.depth_of(parent)
+    tried = np.zeros((K, max(kpd))); hits = np.zeros((K, max(kpd)))
+    lens = []
+    for s in range(steps):
+        cont = target.greedy(seq + [root], K)
+        heads = synth.toy_draft_logits_ranked(cont, target.V, drafts.ranks(rng, kpd), seed * 7919 + s)
+        toks = otree.tree_tokens(otopk.head_topk(heads[None], kpd), [root], parent, rank)[0]
+        pref = node_prefixes(seq, root, toks, parent)
+        base = np.stack([target.logits(p) for p in pref])
+        res = oaccept.accept_greedy(base, toks, parent, rank)
+        on_path = set(res.nodes)
+        for n in range(1, T):
+            if int(parent[n]) in on_path:
+                tried[depth[n] - 1, rank[n]] += 1
+                hits[depth[n] - 1, rank[n]] += n in on_path
+        lens.append(res.accept_len)
+        seq += [root] + res.tokens[:-1]
+        root = res.tokens[-1]
+    return np.array(lens), tried, hits
