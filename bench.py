@@ -119,15 +119,14 @@ def build_step(w, dev):
     q0, k0, v0 = synth.attention_inputs(w, 0, dev)[:3]
     k_all = torch.empty((w.L,) + tuple(k0.shape), dtype=k0.dtype, device=dev)
     v_all = torch.empty_like(k_all)
-    qs = [q0]
-    k_all[0], v_all[0] = k0, v0
-    del k0, v0
+    q_all = torch.empty((w.L,) + tuple(q0.shape), dtype=q0.dtype, device=dev)
+    q_all[0], k_all[0], v_all[0] = q0, k0, v0
+    del q0, k0, v0
     for l in range(1, w.L):
         q, k, v = synth.attention_inputs(w, l, dev)[:3]
-        qs.append(q)
-        k_all[l], v_all[l] = k, v
-        del k, v
-    layers = [(qs[l], k_all[l], v_all[l]) for l in range(w.L)]
+        q_all[l], k_all[l], v_all[l] = q, k, v
+        del q, k, v
+    layers = [(q_all[l], k_all[l], v_all[l]) for l in range(w.L)]
     base = synth.normal((w.B, w.T, w.V), w.base_logit_std, synth.seed_for(w.cfg_id, synth.T_BASE), dev)
     ua = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_UACC), dev)
     us = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_USMP), dev)
@@ -136,7 +135,8 @@ def build_step(w, dev):
     topk = torch.empty((w.B, w.K, tree.kmax), dtype=torch.int32, device=dev)
     toks = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
     pos = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
-    outs = [torch.empty((w.B, w.T, w.Hq, w.D), dtype=torch.bfloat16, device=dev) for _ in range(w.L)]
+    out_all = torch.empty((w.L, w.B, w.T, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    outs = [out_all[l] for l in range(w.L)]
     acc_outs = {tau: (torch.empty(w.B, dtype=torch.int32, device=dev),
                       torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev),
                       torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev))
@@ -147,6 +147,8 @@ def build_step(w, dev):
 
     ws_heads = ws(api.heads_workspace_size(w.B, w.H, w.K, torch.bfloat16))
     ws_attn = ws(api.tree_attention_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.ctx, tree, torch.bfloat16))
+    ws_attn_layers = ws(api.tree_attention_layers_workspace_size(w.L, w.B, w.Hq, w.Hkv, w.D, w.ctx,
+                                                                 tree, torch.bfloat16))
     ws_acc = ws(max(api.accept_workspace_size(w.B, w.V, tree, t) for t in w.temperature))
 
     def stage_heads():
@@ -158,6 +160,10 @@ def build_step(w, dev):
     def stage_attention(l):
         q, k, v = layers[l]
         api.tree_attention(q, k, v, ctx, w.ctx, tree, out=outs[l], ws=ws_attn)
+
+    def stage_attention_batched():  # every layer in one grid (secondary figure)
+        api.tree_attention_layers(q_all, k_all, v_all, ctx, w.ctx, tree, out=out_all,
+                                  ws=ws_attn_layers)
 
     def stage_accept():
         for tau, o in acc_outs.items():
@@ -178,7 +184,8 @@ def build_step(w, dev):
         stage_accept()
 
     keep = dict(hidden=hidden, w1=w1, wlm=wlm, tree=tree, layers=layers, base=base)
-    return step, (stage_heads, stage_candidates, stage_attention, stage_accept, stage_commit), keep
+    return step, (stage_heads, stage_candidates, stage_attention, stage_accept, stage_commit,
+                  stage_attention_batched), keep
 
 
 def _capture(fn):
@@ -221,7 +228,8 @@ def time_gpu(w, args):
     torch.cuda.set_device(dev)
     step, stages, keep = build_step(w, dev)
     torch.cuda.synchronize()
-    stage_heads, stage_candidates, stage_attention, stage_accept, stage_commit = stages
+    (stage_heads, stage_candidates, stage_attention, stage_accept, stage_commit,
+     stage_attention_batched) = stages
 
     run = step if args.eager else _capture(step).replay
     log(f"warmup {args.warmup}, timing {args.steps} steps ({'eager' if args.eager else 'graph'})")
@@ -247,7 +255,8 @@ def time_gpu(w, args):
 
     graphs = {"heads": _capture(stage_heads), "candidates": _capture(stage_candidates),
               "attention": _capture(all_layers), "accept": _capture(stage_accept),
-              "commit": _capture(stage_commit)}
+              "commit": _capture(stage_commit),
+              "attention_batched": _capture(stage_attention_batched)}
     reps = max(5, args.steps)
     stages_us = {n: 1000.0 * _time_replays(g.replay, reps, 3) for n, g in graphs.items()}
     attn_call_us = stages_us["attention"] / w.L
@@ -377,6 +386,12 @@ def main():
         "heads": {"hbm_gbs": round(heads_gbs, 1), "hbm_frac": round(heads_gbs / HBM_PEAK_GBS, 4),
                   "mfma_tflops": round(heads_tflops, 2),
                   "mfma_frac": round(heads_tflops / BF16_MFMA_PEAK_TFLOPS, 5)},
+        "tree_attention_batched": {
+            "us_all_layers": round(stages_us["attention_batched"], 2),
+            "us_per_layer": round(stages_us["attention_batched"] / w.L, 2),
+            "hbm_gbs": round(a_bytes * w.L / (stages_us["attention_batched"] * 1e-6) / 1e9, 1),
+            "hbm_frac": round(a_bytes * w.L / (stages_us["attention_batched"] * 1e-6) / 1e9
+                              / HBM_PEAK_GBS, 4)},
         "stages_us": {k: round(v, 2) for k, v in stages_us.items()},
         "wall_s_timed": round(wall_s, 4),
     }

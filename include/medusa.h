@@ -5,7 +5,8 @@
  * One Medusa verify step has four stages, each one call here:
  *   medusa_heads            K residual-SiLU heads + vocab projections
  *   medusa_tree_candidates  per-head top-k, candidate tree tokens, positions
- *   medusa_tree_attention   tree-masked attention of one layer (split-KV)
+ *   medusa_tree_attention   tree-masked attention of one layer (split-KV);
+ *                           _layers: every layer in one grid
  *   medusa_accept_paths     longest accepted root-to-leaf path (greedy or
  *                           rejection sampling)
  * and one call closes the step:
@@ -211,6 +212,27 @@ int medusa_tree_attention(const void* q, const void* k_cache, const void* v_cach
                           int B, int Hq, int Hkv, int D, int S_cap, float scale,
                           medusa_dtype_t dt, void* out, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/* Every layer of the target in one call (same tree, same ctx_len): layer l
+ * reads q + l * q_layer_stride, k_cache/v_cache + l * kv_layer_stride and
+ * writes out + l * out_layer_stride (strides in ELEMENTS, each at least one
+ * layer's extent and a multiple of 16 bytes; layouts within a layer as
+ * above).  Same operation as L calls of medusa_tree_attention (the layers
+ * are independent, P1, section "트리 어텐션"), with one grid for all of them
+ * so that short contexts still fill the chip; the split count is planned for
+ * L * B sequences, so the workspace is sized by the _layers size call.
+ * Errors as medusa_tree_attention, plus MEDUSA_EINVAL for L < 1 or strides
+ * that overlap layers. */
+size_t medusa_tree_attention_layers_workspace_size(int L, int B, int Hq, int Hkv, int D,
+                                                   int ctx_max, const medusa_tree_t* tree,
+                                                   medusa_dtype_t dt);
+
+int medusa_tree_attention_layers(const void* q, const void* k_cache, const void* v_cache,
+                                 int64_t q_layer_stride, int64_t kv_layer_stride,
+                                 int64_t out_layer_stride, int L, const int32_t* ctx_len,
+                                 int ctx_max, const medusa_tree_t* tree, int B, int Hq, int Hkv,
+                                 int D, int S_cap, float scale, medusa_dtype_t dt, void* out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Stage 6: path acceptance

@@ -183,6 +183,46 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     return out
 
 
+def tree_attention_layers_workspace_size(L, B, Hq, Hkv, D, ctx_max, tree: Tree, dtype) -> int:
+    return _lib.load().medusa_tree_attention_layers_workspace_size(
+        L, B, Hq, Hkv, D, ctx_max, tree.handle, F32 if dtype == torch.float32 else BF16)
+
+
+def tree_attention_layers(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          ctx_len: torch.Tensor, ctx_max: int, tree: Tree,
+                          scale: Optional[float] = None, out=None, ws=None, stream=None):
+    """Every layer in one call: q [L,B,T,Hq,D]; k_cache/v_cache [L,B,Hkv,S_cap,D]
+    -> out [L,B,T,Hq,D].  Each layer's block must be contiguous; the layer
+    dimension may be strided."""
+    lib = _lib.load()
+    L, B, T, Hq, D = q.shape
+    Hkv, S_cap = k_cache.shape[2], k_cache.shape[3]
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same shape and strides")
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+
+    def layered(t):  # the layer dimension may be strided, each layer's block not
+        if not t[0].is_contiguous():
+            raise ValueError("each layer's block must be contiguous")
+        return ctypes.c_void_p(t.data_ptr())
+
+    nbytes = lib.medusa_tree_attention_layers_workspace_size(L, B, Hq, Hkv, D, ctx_max,
+                                                             tree.handle, dt)
+    ws, nb = _workspace(nbytes, q.device, ws)
+    _check(lib.medusa_tree_attention_layers(
+        layered(q), layered(k_cache), layered(v_cache), q.stride(0), k_cache.stride(0),
+        out.stride(0), L,
+        _ptr(ctx_len), ctx_max, tree.handle, B, Hq, Hkv, D, S_cap, float(scale), dt, layered(out),
+        _ptr(ws), nb, _stream(stream)))
+    return out
+
+
 def accept_workspace_size(B, V, tree: Tree, temperature: float) -> int:
     return _lib.load().medusa_accept_workspace_size(B, V, tree.handle, float(temperature))
 

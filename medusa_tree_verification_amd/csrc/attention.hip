@@ -77,6 +77,8 @@ struct AttnArgs {
   const int32_t* ctx;
   const uint64_t* mask;  // [T][W]
   int W, B, T, Hq, Hkv, G, S_cap;
+  int L;                                       // layers in this call
+  int64_t q_lstride, kv_lstride, out_lstride;  // elements between layers
   int QR, QRpad, QC, NS, chunk;
   int tasks, per_xcd;
   float scale_log2;
@@ -126,11 +128,15 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
   const int task = (id & 7) * a.per_xcd + (id >> 3);
   if (task >= a.tasks) return;  // whole workgroup leaves before any barrier
   const int split = task % a.NS;
-  const int rest = task / a.NS;  // = bh * QC + qc
+  const int rest = task / a.NS;  // = lbh * QC + qc
   const int qc = rest % a.QC;
-  const int bh = rest / a.QC;
+  const int lbh = rest / a.QC;   // = layer * B * Hkv + bh
+  const int bh = lbh % (a.B * a.Hkv);
+  const int layer = lbh / (a.B * a.Hkv);
   const int b = bh / a.Hkv;
   const int kvh = bh % a.Hkv;
+  const uint16_t* qL = a.q + layer * a.q_lstride;
+  uint16_t* outL = a.out + layer * a.out_lstride;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,7 +157,8 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
   // ---- staging roles: waves 8-9 load K rows, waves 10-11 V ----
   const bool k_role = wave < 10;
   const int rt = tid - (k_role ? 512 : 640);  // 0..127 within the role
-  const uint16_t* gbase = (k_role ? a.k : a.v) + static_cast<int64_t>(bh) * a.S_cap * D;
+  const uint16_t* gbase =
+      (k_role ? a.k : a.v) + layer * a.kv_lstride + static_cast<int64_t>(bh) * a.S_cap * D;
   int goff[8];  // byte offsets of this thread's 8 loads within a block
   int lds_w;    // this thread's LDS store offset within a slot
   if (k_role) {
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
   const int row0 = qc * ROWS_WG;
   auto q_ptr = [&](int r, int ch) __attribute__((always_inline)) {
     const int node = r / a.G, gq = r % a.G;
-    return a.q + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + ch * 8;
+    return qL + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + ch * 8;
   };
   bf16x8 qf[QREG ? 4 : 1];
   uint64_t* smask = reinterpret_cast<uint64_t*>(smem + a.lds_mask);
@@ -416,7 +423,7 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
     if (a.NS == 1) {
       const float inv = 1.0f / l_run[t];
       const int node = r / a.G, gq = r % a.G;
-      uint16_t* op = a.out + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D;
+      uint16_t* op = outL + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const f32x4 v = o[t][dt] * inv;
@@ -426,7 +433,7 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
     } else {
       // the split's output normalised by its own sum (bf16), with its max and
       // sum in fp32; a split that saw no key has sum 0 and writes zeros
-      const int64_t prow = (static_cast<int64_t>(split) * BH + bh) * a.QRpad + r;
+      const int64_t prow = (static_cast<int64_t>(split) * a.L * BH + lbh) * a.QRpad + r;
       uint16_t* po = a.part_o + prow * D;
       const float inv = l_run[t] > 0.f ? 1.0f / l_run[t] : 0.f;
 #pragma unroll
@@ -448,12 +455,13 @@ __global__ __launch_bounds__(256) void merge_splits(AttnArgs a) {
   const int lane = threadIdx.x & 31;  // lane within the row's half-wave
   const int BH = a.B * a.Hkv;
   const int64_t gr = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
-  const bool live = gr < static_cast<int64_t>(BH) * a.QR;  // both halves reach the shuffles
+  const bool live = gr < static_cast<int64_t>(a.L) * BH * a.QR;  // both halves reach the shuffles
   const int64_t grc = live ? gr : 0;
-  const int bh = static_cast<int>(grc / a.QR);
+  const int lbh = static_cast<int>(grc / a.QR);  // = layer * B * Hkv + bh
+  const int bh = lbh % BH, layer = lbh / BH;
   const int r = static_cast<int>(grc % a.QR);
-  const int64_t stride = static_cast<int64_t>(BH) * a.QRpad;  // rows between splits
-  const int64_t row = static_cast<int64_t>(bh) * a.QRpad + r;
+  const int64_t stride = static_cast<int64_t>(a.L) * BH * a.QRpad;  // rows between splits
+  const int64_t row = static_cast<int64_t>(lbh) * a.QRpad + r;
   const int ns = a.NS;
   // lane s holds splits s and s + 32
   float2 ml0 = make_float2(-INFINITY, 0.f), ml1 = make_float2(-INFINITY, 0.f);
@@ -490,7 +498,8 @@ __global__ __launch_bounds__(256) void merge_splits(AttnArgs a) {
   const float inv = 1.0f / L;
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   const int node = r / a.G, gq = r % a.G;
-  uint16_t* op = a.out + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + 4 * lane;
+  uint16_t* op = a.out + layer * a.out_lstride +
+                 ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + 4 * lane;
   *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv));
 }
 
@@ -673,22 +682,17 @@ int launch_cfg(const AttnArgs& a, int grid, int lds, hipStream_t s) {
 
 }  // namespace
 
-extern "C" size_t medusa_tree_attention_workspace_size(int B, int Hq, int Hkv, int D_, int ctx_max,
-                                                       const medusa_tree_t* tree,
-                                                       medusa_dtype_t dt) {
-  if (!tree || B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || ctx_max < 0) return 0;
-  if (dt != MEDUSA_BF16 || D_ != D) return 0;
-  return make_plan(B, Hq, Hkv, ctx_max, tree->T, tree->W).ws_bytes;
-}
+namespace {
 
-extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const void* v_cache,
-                                     const int32_t* ctx_len, int ctx_max, const medusa_tree_t* tree,
-                                     int B, int Hq, int Hkv, int D_, int S_cap, float scale,
-                                     medusa_dtype_t dt, void* out, void* ws, size_t ws_bytes,
-                                     hipStream_t stream) {
-  clear_error();
+// one or several layers (layer l at base + l * stride elements)
+int attention_launch(const void* q, const void* k_cache, const void* v_cache, int64_t q_lstride,
+                     int64_t kv_lstride, int64_t out_lstride, int L, const int32_t* ctx_len,
+                     int ctx_max, const medusa_tree_t* tree, int B, int Hq, int Hkv, int D_,
+                     int S_cap, float scale, medusa_dtype_t dt, void* out, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
   int rc = check_tree(tree);
   if (rc) return rc;
+  MEDUSA_CHECK_ARG(L >= 1, "L=%d must be >= 1", L);
   MEDUSA_CHECK_ARG(q && k_cache && v_cache && ctx_len && out, "tensor arguments must be non-NULL");
   MEDUSA_CHECK_ARG(B >= 1 && Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0,
                    "need B >= 1 and Hq (%d) a positive multiple of Hkv (%d)", Hq, Hkv);
@@ -720,9 +724,17 @@ extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const v
     f.scale = scale;
     f.out = static_cast<float*>(out);
     const int64_t rows = static_cast<int64_t>(B) * tree->T * Hq;
-    hipLaunchKernelGGL(tree_attn_f32, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0,
-                       stream, f);
-    return check_launch("tree attention (f32)");
+    for (int l = 0; l < L; ++l) {  // small configurations: one launch per layer
+      f.q = static_cast<const float*>(q) + l * q_lstride;
+      f.k = static_cast<const float*>(k_cache) + l * kv_lstride;
+      f.v = static_cast<const float*>(v_cache) + l * kv_lstride;
+      f.out = static_cast<float*>(out) + l * out_lstride;
+      hipLaunchKernelGGL(tree_attn_f32, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0,
+                         stream, f);
+      rc = check_launch("tree attention (f32)");
+      if (rc) return rc;
+    }
+    return MEDUSA_OK;
   }
   MEDUSA_CHECK_ARG(dt == MEDUSA_BF16, "unknown dtype %d", static_cast<int>(dt));
   if (D_ != D) {
@@ -730,7 +742,7 @@ extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const v
     return MEDUSA_EUNSUPPORTED;
   }
   MEDUSA_CHECK_ARG(S_cap < (1 << 23), "S_cap=%d too large (K/V byte offsets are 32-bit)", S_cap);
-  const Plan p = make_plan(B, Hq, Hkv, ctx_max, tree->T, tree->W);
+  const Plan p = make_plan(L * B, Hq, Hkv, ctx_max, tree->T, tree->W);
   if (p.NS > 1 && (!ws || ws_bytes < p.ws_bytes || !aligned256(ws))) {
     set_error("tree attention workspace: need %zu bytes, 256-byte aligned (got %zu at %p)",
               p.ws_bytes, ws_bytes, ws);
@@ -753,12 +765,16 @@ extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const v
   a.Hkv = Hkv;
   a.G = p.G;
   a.S_cap = S_cap;
+  a.L = L;
+  a.q_lstride = q_lstride;
+  a.kv_lstride = kv_lstride;
+  a.out_lstride = out_lstride;
   a.QR = p.QR;
   a.QRpad = p.QRpad;
   a.QC = p.QC;
   a.NS = p.NS;
   a.chunk = p.chunk;
-  a.tasks = B * Hkv * p.QC * p.NS;
+  a.tasks = L * B * Hkv * p.QC * p.NS;
   a.per_xcd = (a.tasks + 7) / 8;
   a.scale_log2 = scale * LOG2E;
   a.out = static_cast<uint16_t*>(out);
@@ -776,7 +792,59 @@ extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const v
     default: rc = launch_cfg<2>(a, grid, p.lds_bytes, stream); break;
   }
   if (rc || p.NS == 1) return rc;
-  const int64_t rows = static_cast<int64_t>(B) * Hkv * p.QR;
+  const int64_t rows = static_cast<int64_t>(L) * B * Hkv * p.QR;
   hipLaunchKernelGGL(merge_splits, dim3(static_cast<unsigned>((rows + 7) / 8)), dim3(256), 0, stream, a);
   return check_launch("tree attention split merge");
+}
+
+}  // namespace
+
+extern "C" size_t medusa_tree_attention_workspace_size(int B, int Hq, int Hkv, int D_, int ctx_max,
+                                                       const medusa_tree_t* tree,
+                                                       medusa_dtype_t dt) {
+  if (!tree || B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || ctx_max < 0) return 0;
+  if (dt != MEDUSA_BF16 || D_ != D) return 0;
+  return make_plan(B, Hq, Hkv, ctx_max, tree->T, tree->W).ws_bytes;
+}
+
+extern "C" int medusa_tree_attention(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* ctx_len, int ctx_max, const medusa_tree_t* tree,
+                                     int B, int Hq, int Hkv, int D_, int S_cap, float scale,
+                                     medusa_dtype_t dt, void* out, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  clear_error();
+  return attention_launch(q, k_cache, v_cache, 0, 0, 0, 1, ctx_len, ctx_max, tree, B, Hq, Hkv, D_,
+                          S_cap, scale, dt, out, ws, ws_bytes, stream);
+}
+
+extern "C" size_t medusa_tree_attention_layers_workspace_size(int L, int B, int Hq, int Hkv, int D_,
+                                                              int ctx_max, const medusa_tree_t* tree,
+                                                              medusa_dtype_t dt) {
+  if (L < 1 || B < 1 || static_cast<int64_t>(L) * B >= (1ll << 31)) return 0;
+  return medusa_tree_attention_workspace_size(L * B, Hq, Hkv, D_, ctx_max, tree, dt);
+}
+
+extern "C" int medusa_tree_attention_layers(const void* q, const void* k_cache, const void* v_cache,
+                                            int64_t q_layer_stride, int64_t kv_layer_stride,
+                                            int64_t out_layer_stride, int L, const int32_t* ctx_len,
+                                            int ctx_max, const medusa_tree_t* tree, int B, int Hq,
+                                            int Hkv, int D_, int S_cap, float scale,
+                                            medusa_dtype_t dt, void* out, void* ws, size_t ws_bytes,
+                                            hipStream_t stream) {
+  clear_error();
+  MEDUSA_CHECK_ARG(L >= 1 && static_cast<int64_t>(L) * B * Hkv < (1ll << 28), "L=%d out of range", L);
+  const int esize = dt == MEDUSA_F32 ? 4 : 2;
+  const int64_t q_elems = static_cast<int64_t>(B) * (tree ? tree->T : 0) * Hq * D_;
+  const int64_t kv_elems = static_cast<int64_t>(B) * Hkv * S_cap * D_;
+  MEDUSA_CHECK_ARG(L == 1 || (q_layer_stride >= q_elems && out_layer_stride >= q_elems &&
+                              kv_layer_stride >= kv_elems),
+                   "layer strides (%lld, %lld, %lld) smaller than one layer",
+                   static_cast<long long>(q_layer_stride), static_cast<long long>(kv_layer_stride),
+                   static_cast<long long>(out_layer_stride));
+  MEDUSA_CHECK_ARG((q_layer_stride * esize) % 16 == 0 && (kv_layer_stride * esize) % 16 == 0 &&
+                       (out_layer_stride * esize) % 16 == 0,
+                   "layer strides must keep 16-byte alignment");
+  return attention_launch(q, k_cache, v_cache, q_layer_stride, kv_layer_stride, out_layer_stride, L,
+                          ctx_len, ctx_max, tree, B, Hq, Hkv, D_, S_cap, scale, dt, out, ws,
+                          ws_bytes, stream);
 }
