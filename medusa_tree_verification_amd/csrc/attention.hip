@@ -16,11 +16,17 @@
 //   roles that meet at one barrier per 64-key block:
 //   - 4 staging waves stream the split's K/V through buffer loads into
 //     registers, NREG blocks ahead of use, and write each block into one of
-//     two LDS slots: K rows padded to 272 bytes; V transposed (rows = d, 144
-//     bytes) with the 8 keys a lane feeds to one P.V MFMA k-step in one
-//     16-byte granule, granules XOR-swizzled by d/16.  Every LDS access of
-//     the kernel is free of bank conflicts.  Memory stalls of these waves do
-//     not hold up the arithmetic.
+//     two LDS slots: K rows of 256 bytes with their 16-byte chunks
+//     XOR-swizzled by the row; V transposed (rows = d, 128 bytes) with the 8
+//     keys a lane feeds to one P.V MFMA k-step in one 16-byte granule,
+//     granules XOR-swizzled by a function of d.  Memory stalls of these
+//     waves do not hold up the arithmetic.
+//   LDS banks (gfx950, measured with the bank-conflict counter): a 16-byte
+//   read is served in 4 passes of 16 lanes over 64 four-byte banks, lanes
+//   {0-3, 12-15, 20-27} (and the same +32) sharing a pass, the others the
+//   other; a 16-byte write in 8 passes of 8 consecutive lanes over 32 banks.
+//   Both swizzles make every read and write of the kernel conflict-free
+//   under that rule.
 //   - 8 compute waves: wave w takes query tiles (16 rows) w%4, w%4 + 4, ...
 //     and the 32-key half w/4 of every block, keeping its own online-softmax
 //     state; the two halves are merged through LDS at the end (fixed order).
@@ -55,15 +61,25 @@ namespace {
 constexpr int D = 128;
 constexpr int KB = 64;                      // keys per block (one wave's unit of work)
 constexpr int GROWB = D * 2;                // bytes per K/V row in HBM
-constexpr int KROWB = GROWB + 16;           // K (and staged Q) row in LDS, padded: 272
-constexpr int K_TILE = KB * KROWB;          // 17408
-constexpr int VROWB = KB * 2 + 16;          // V^T row (one d, 64 keys) in LDS, padded: 144
-constexpr int V_TILE = D * VROWB;           // 18432
-constexpr int BLK_BYTES = K_TILE + V_TILE;  // 35840
+constexpr int KROWB = GROWB;                // K (and staged Q) row in LDS: 256
+constexpr int K_TILE = KB * KROWB;          // 16384
+constexpr int VROWB = KB * 2;               // V^T row (one d, 64 keys) in LDS: 128
+constexpr int V_TILE = D * VROWB;           // 16384
+constexpr int BLK_BYTES = K_TILE + V_TILE;  // 32768
+
+// K / staged Q tile: 16-byte chunk c of row r lives at r * 256 + 16 * (c ^ (r & 15)).
+__device__ __forceinline__ int kq_off(int r, int c) { return r * KROWB + 16 * (c ^ (r & 15)); }
+// V^T tile: granule G (8 keys) of row d lives at d * 128 + 16 * (G ^ vswz(d)),
+// vswz(d) = rot3((d >> 3) & 7) ^ 4 * (bit 1 of d ^ bit 2 of d), rot3 rotating
+// 3 bits left by one.
+__device__ __forceinline__ constexpr int rot3(int x) { return ((x << 1) | (x >> 2)) & 7; }
 constexpr int NSLOT = 2;                    // LDS slots (blocks staged at once)
 constexpr int NREG = 2;                     // blocks in flight in staging registers
 constexpr int MERGE_BYTES = 8 * 64 * 16 + 64 * 8;  // one wave-tile's O, max and sum
 constexpr int MAX_SPLITS = 64;
+// exponents may exceed the reference by up to this much (log2 units), so
+// unnormalised probabilities stay <= 256
+constexpr float RESCALE_SLACK = 8.0f;
 constexpr int LDS_MAX = 160 * 1024;         // LDS of one CU              // the merge keeps one split per lane
 constexpr int RSRC_WORD3 = 0x00020000;      // raw buffer, 32-bit data format
 constexpr float LOG2E = 1.4426950408889634f;
@@ -159,21 +175,26 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
   const int rt = tid - (k_role ? 512 : 640);  // 0..127 within the role
   const uint16_t* gbase =
       (k_role ? a.k : a.v) + layer * a.kv_lstride + static_cast<int64_t>(bh) * a.S_cap * D;
-  int goff[8];  // byte offsets of this thread's 8 loads within a block
-  int lds_w;    // this thread's LDS store offset within a slot
+  int goff[8];   // byte offsets of this thread's 8 loads within a block
+  int lds_w;     // this thread's LDS store offset within a slot (K: even loads)
+  int lds_w_odd; // K: odd loads (their row is 8 further, which flips bit 3 of the swizzle)
   if (k_role) {
-    // chunk c = rt + 128*i of the block: key row c/16, 16-byte chunk c%16
-    const int base = (rt >> 4) * GROWB + (rt & 15) * 16;
+    // load i: key row rt/16 + 8i, 16-byte chunk rt%16
+    const int r = rt >> 4, c = rt & 15;
+    const int base = r * GROWB + c * 16;
 #pragma unroll
     for (int i = 0; i < 8; ++i) goff[i] = base + 8 * i * GROWB;
-    lds_w = (rt >> 4) * KROWB + (rt & 15) * 16;
+    lds_w = kq_off(r, c);
+    lds_w_odd = kq_off(r + 8, c) - 8 * KROWB;
   } else {
-    // d-octet o of the 8 keys {4g..4g+3, 16+4g..16+4g+3} of half h
+    // d-octet o of the 8 keys {4g..4g+3, 16+4g..16+4g+3} of half h: row
+    // d = 8o + dd of V^T, granule 4h + g
     const int o = rt & 15, g = (rt >> 4) & 3, h = rt >> 6;
     const int base = (h * 32 + 4 * g) * GROWB + o * 16;
 #pragma unroll
     for (int i = 0; i < 8; ++i) goff[i] = base + (i < 4 ? i : 12 + i) * GROWB;
-    lds_w = K_TILE + 8 * o * VROWB + 16 * ((h * 4 + g) ^ (o >> 1));
+    lds_w = K_TILE + 8 * o * VROWB + 16 * ((h * 4 + g) ^ rot3(o & 7));
+    lds_w_odd = 0;
   }
   // a block's loads through a buffer resource that ends at the split's end:
   // reads of keys >= k_end return zeros (never the unused cache slots)
@@ -187,10 +208,10 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
     for (int i = 0; i < 8; ++i) x[i] = bload16(r, goff[i]);
   };
   auto lds_put = [&](const uint4 (&x)[8], char* slot) __attribute__((always_inline)) {
-    char* p = slot + lds_w;
     if (k_role) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(p + 8 * i * KROWB) = x[i];
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint4*>(slot + 8 * i * KROWB + ((i & 1) ? lds_w_odd : lds_w)) = x[i];
     } else {
       // row d = 8o + dd of V^T: element dd of each of the 8 keys, in k-slot order
 #pragma unroll
@@ -201,7 +222,8 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
         w.y = __builtin_amdgcn_perm(word(x[3], dd >> 1), word(x[2], dd >> 1), sel);
         w.z = __builtin_amdgcn_perm(word(x[5], dd >> 1), word(x[4], dd >> 1), sel);
         w.w = __builtin_amdgcn_perm(word(x[7], dd >> 1), word(x[6], dd >> 1), sel);
-        *reinterpret_cast<uint4*>(p + dd * VROWB) = w;
+        // vswz(8o + dd) = rot3(o & 7) ^ 4 * (bit 1 of dd ^ bit 2 of dd)
+        *reinterpret_cast<uint4*>(slot + (lds_w ^ ((((dd >> 1) ^ (dd >> 2)) & 1) ? 64 : 0)) + dd * VROWB) = w;
       }
     }
   };
@@ -254,14 +276,14 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
     if constexpr (QREG) {
       const int r = min(row0 + qw * 16 + l16, a.QR - 1);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(ldg16(q_ptr(r, grp * 4 + s)));
+      for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(ldg16(q_ptr(r, 4 * s + grp)));
     } else {
       constexpr int Q_PER_THREAD = ROWS_WG * 16 / 512;
 #pragma unroll
       for (int u = 0; u < Q_PER_THREAD; ++u) {
         const int idx = tid + 512 * u;
         const uint4 v = ldg16(q_ptr(min(row0 + idx / 16, a.QR - 1), idx % 16));
-        *reinterpret_cast<uint4*>(smem + a.lds_q + (idx / 16) * KROWB + (idx % 16) * 16) =
+        *reinterpret_cast<uint4*>(smem + a.lds_q + kq_off(idx / 16, idx % 16)) =
             (row0 + idx / 16 < a.QR) ? v : make_uint4(0, 0, 0, 0);
       }
     }
@@ -282,30 +304,39 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
     qnode[t] = r < a.QR ? r / a.G : 0;
   }
   f32x4 o[QTW][8];
-  float m_run[QTW], l_run[QTW];
+  // per query: m_run the largest scaled score seen when the reference last
+  // moved (-inf before any visible key), mu the reference the exponents use
+  // (m_run, or 0 while m_run is -inf), l_run the sum of exp2(s - mu) and o
+  // the matching weighted sum of values
+  float m_run[QTW], mu[QTW], l_run[QTW];
 #pragma unroll
   for (int t = 0; t < QTW; ++t) {
     m_run[t] = -INFINITY;
+    mu[t] = 0.f;
     l_run[t] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const char* sq = smem + a.lds_q + l16 * KROWB + grp * 64;
-  // V^T read offsets: granule (4h + grp) ^ dt of row dt*16 + l16
-  int vx[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) vx[c] = K_TILE + l16 * VROWB + 16 * (grp ^ c);
+  // k-step s feeds lane group grp the 16-byte d-chunk 4s + grp of its K and
+  // Q rows (a permutation of d shared by both operands); chunk 4s + grp of
+  // row r (r % 16 = l16) sits at 16 * ((4s + grp) ^ l16) = kx0 ^ 64s
+  const int kx0 = 16 * (grp ^ l16);
+  const char* sq = smem + a.lds_q + l16 * KROWB;
+  // V^T: row dt*16 + l16, granule 4*half + grp at
+  // (vbase ^ 16 * rot3(2dt & 7)) + dt * 16 * VROWB
+  const int vbase = K_TILE + l16 * VROWB +
+                    16 * ((4 * half + grp) ^ rot3(l16 >> 3) ^ (4 * (((l16 >> 1) ^ (l16 >> 2)) & 1)));
 
   // this wave's 32-key half of a 64-key block (keys kh .. kh+31)
   auto compute = [&](const char* blk, int kh) __attribute__((always_inline)) {
     f32x4 sc[QTW][2];
-    const char* kr = blk + (half * 32 + l16) * KROWB + grp * 64;
+    const char* kr = blk + (half * 32 + l16) * KROWB;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       bf16x8 kf[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + st * 16 * KROWB + 16 * s));
+        kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + st * 16 * KROWB + (kx0 ^ (64 * s))));
 #pragma unroll
       for (int t = 0; t < QTW; ++t) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -313,7 +344,7 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
         for (int s = 0; s < 4; ++s) {
           bf16x8 q;
           if constexpr (QREG) q = qf[s];
-          else q = as_bf16x8(*reinterpret_cast<const uint4*>(sq + (qw + 4 * t) * 16 * KROWB + 16 * s));
+          else q = as_bf16x8(*reinterpret_cast<const uint4*>(sq + (qw + 4 * t) * 16 * KROWB + (kx0 ^ (64 * s))));
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], q, acc, 0, 0, 0);
         }
         sc[t][st] = acc;
@@ -336,34 +367,46 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
         }
       }
     }
-    uint4 pb[QTW];
+    // the reference mu moves only when a score passes it by more than
+    // RESCALE_SLACK (log2 units): then, and only then, the block max is
+    // reduced over the 4 lane rows and the state rescaled
+    float lm[QTW];
+    bool over = false;
 #pragma unroll
     for (int t = 0; t < QTW; ++t) {
-      float mx = fmaxf(fmaxf(fmaxf(sc[t][0][0], sc[t][0][1]), fmaxf(sc[t][0][2], sc[t][0][3])),
-                       fmaxf(fmaxf(sc[t][1][0], sc[t][1][1]), fmaxf(sc[t][1][2], sc[t][1][3])));
-      mx = rows_max(mx);
-      const float mnew = fmaxf(m_run[t], mx * a.scale_log2);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[t] - muse);
-      m_run[t] = mnew;
-      float p[2][4];
+      lm[t] = fmaxf(fmaxf(fmaxf(sc[t][0][0], sc[t][0][1]), fmaxf(sc[t][0][2], sc[t][0][3])),
+                    fmaxf(fmaxf(sc[t][1][0], sc[t][1][1]), fmaxf(sc[t][1][2], sc[t][1][3])));
+      over |= lm[t] * a.scale_log2 > m_run[t] + RESCALE_SLACK;
+    }
+    if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[st][e] = __builtin_amdgcn_exp2f(fmaf(sc[t][st][e], a.scale_log2, -muse));
-      l_run[t] = fmaf(l_run[t], alpha, ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-                                           ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
-      pb[t] = make_uint4(pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
-                         pack_bf16(p[1][2], p[1][3]));
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // some query's max moved
+      for (int t = 0; t < QTW; ++t) {
+        const float mnew = fmaxf(m_run[t], rows_max(lm[t]) * a.scale_log2);
+        const float mu_new = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - mu_new);  // 0 before any key
+        m_run[t] = mnew;
+        mu[t] = mu_new;
+        l_run[t] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
       }
     }
+    uint4 pb[QTW];
+#pragma unroll
+    for (int t = 0; t < QTW; ++t) {
+      float p[2][4];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[st][e] = __builtin_amdgcn_exp2f(fmaf(sc[t][st][e], a.scale_log2, -mu[t]));
+      l_run[t] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+      pb[t] = make_uint4(pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
+                         pack_bf16(p[1][2], p[1][3]));
+    }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const bf16x8 va = as_bf16x8(*reinterpret_cast<const uint4*>(
-          blk + vx[dt & 3] + dt * 16 * VROWB + 64 * ((half ^ (dt >> 2)) & 1)));
+          blk + (vbase ^ (16 * rot3((2 * dt) & 7))) + dt * 16 * VROWB));
 #pragma unroll
       for (int t = 0; t < QTW; ++t)
         o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(pb[t]), o[t][dt], 0, 0, 0);
