@@ -50,6 +50,7 @@
 //   i % 8), which keeps their partials in one L2.
 #include <cmath>
 #include <cstdlib>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -73,7 +74,7 @@ __device__ __forceinline__ int kq_off(int r, int c) { return r * KROWB + 16 * (c
 // vswz(d) = rot3((d >> 3) & 7) ^ 4 * (bit 1 of d ^ bit 2 of d), rot3 rotating
 // 3 bits left by one.
 __device__ __forceinline__ constexpr int rot3(int x) { return ((x << 1) | (x >> 2)) & 7; }
-constexpr int NSLOT = 2;                    // LDS slots (blocks staged at once)
+constexpr int NSLOT = 3;                    // LDS slots (blocks staged at once)
 constexpr int NREG = 2;                     // blocks in flight in staging registers
 constexpr int MERGE_BYTES = 8 * 64 * 16 + 64 * 8;  // one wave-tile's O, max and sum
 constexpr int MAX_SPLITS = 64;
@@ -250,14 +251,17 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
     if (nblk > 0) lds_put(R[0], ring);
     gload(R[0], NREG);
     __syncthreads();
+    int ws = 1;  // slot of block blk + j + 1
     for (int blk = 0; blk < nblk; blk += NREG) {
 #pragma unroll
       for (int j = 0; j < NREG; ++j) {
-        if (blk + j + 1 < nblk) lds_put(R[(j + 1) % NREG], ring + ((blk + j + 1) & 1) * BLK_BYTES);
+        if (blk + j + 1 < nblk) lds_put(R[(j + 1) % NREG], ring + ws * BLK_BYTES);
+        ws = ws == NSLOT - 1 ? 0 : ws + 1;
         gload(R[(j + 1) % NREG], blk + j + 1 + NREG);
         __syncthreads();
       }
     }
+    __syncthreads();  // the second-half waves' last P.V
     __syncthreads();  // the compute waves' merge of the two key halves
     return;
   }
@@ -327,8 +331,9 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
   const int vbase = K_TILE + l16 * VROWB +
                     16 * ((4 * half + grp) ^ rot3(l16 >> 3) ^ (4 * (((l16 >> 1) ^ (l16 >> 2)) & 1)));
 
-  // this wave's 32-key half of a 64-key block (keys kh .. kh+31)
-  auto compute = [&](const char* blk, int kh) __attribute__((always_inline)) {
+  // scores and probabilities of this wave's 32-key half of a 64-key block
+  // (keys kh .. kh+31), packed as the P.V operand
+  auto qk_softmax = [&](const char* blk, int kh, uint4 (&pb)[QTW]) __attribute__((always_inline)) {
     f32x4 sc[QTW][2];
     const char* kr = blk + (half * 32 + l16) * KROWB;
 #pragma unroll
@@ -391,7 +396,6 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
         for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
       }
     }
-    uint4 pb[QTW];
 #pragma unroll
     for (int t = 0; t < QTW; ++t) {
       float p[2][4];
@@ -403,6 +407,9 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
       pb[t] = make_uint4(pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
                          pack_bf16(p[1][2], p[1][3]));
     }
+  };
+  // O^T += V^T P^T over the same 32 keys
+  auto pv = [&](const char* blk, const uint4 (&pb)[QTW]) __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const bf16x8 va = as_bf16x8(*reinterpret_cast<const uint4*>(
@@ -413,15 +420,49 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
     }
   };
 
-  __syncthreads();
-  for (int blk = 0; blk < nblk; blk += NREG) {
+  // The first-half waves finish each block in its own interval; the
+  // second-half waves run one stage behind on P.V (block i-1's P.V, then
+  // block i's scores), so on every SIMD one wave's softmax overlaps the
+  // other's MFMAs.  Block i-1 stays in its slot through interval i: three
+  // slots, the third being written by the staging waves.
+  auto block_loop = [&](auto skew_tag) __attribute__((always_inline)) {
+    constexpr bool SKEW = decltype(skew_tag)::value;
+    uint4 pb_prev[QTW];
+    const char* slot_prev = ring;
+    bool have_prev = false;
+    int rs = 0;  // slot of block blk + j
+    for (int blk = 0; blk < nblk; blk += NREG) {
 #pragma unroll
-    for (int j = 0; j < NREG; ++j) {
-      const int kh = k_begin + (blk + j) * KB + 32 * half;
-      if (blk + j < nblk && kh < k_end) compute(ring + ((blk + j) & 1) * BLK_BYTES, kh);
-      __syncthreads();
+      for (int j = 0; j < NREG; ++j) {
+        const char* slot = ring + rs * BLK_BYTES;
+        rs = rs == NSLOT - 1 ? 0 : rs + 1;
+        const int kh = k_begin + (blk + j) * KB + 32 * half;
+        const bool live = blk + j < nblk && kh < k_end;
+        if constexpr (!SKEW) {
+          if (live) {
+            uint4 pb[QTW];
+            qk_softmax(slot, kh, pb);
+            pv(slot, pb);
+          }
+        } else {
+          if (have_prev) pv(slot_prev, pb_prev);
+          have_prev = live;
+          if (live) {
+            qk_softmax(slot, kh, pb_prev);
+            slot_prev = slot;
+          }
+        }
+        __syncthreads();
+      }
     }
-  }
+    if constexpr (SKEW) {
+      if (have_prev) pv(slot_prev, pb_prev);
+    }
+  };
+  __syncthreads();
+  if (half == 0) block_loop(std::false_type{});
+  else block_loop(std::true_type{});
+  __syncthreads();  // no wave reads the ring past this point
 
   // full per-query sums (each lane row holds a quarter of the keys)
 #pragma unroll
@@ -682,24 +723,14 @@ Plan make_plan(int B, int Hq, int Hkv, int ctx_max, int T, int W) {
   const int base = B * Hkv * p.QC;
   int ns = env_int("MEDUSA_ATTN_SPLITS", 0);
   if (ns <= 0) {
-    // pick the split count minimising rounds x (fixed cost + blocks per
-    // split) + a cost per split (its partial is written, merged and read),
-    // counting the workgroups all CUs hold at once; in units of one block
+    // the most splits whose workgroups all run in one round of the
+    // resident slots (a second, partly filled round costs more than longer
+    // splits do, and fewer splits leave CUs idle); at least one block each
     const int slots = cu_count() * occupancy(p.QTW, p.lds_bytes);
-    const double fixed_blocks = 1.5;  // prologue and epilogue
-    const double per_split = 0.5;
-    double best = 1e300;
-    ns = 1;
-    const int max_ns = (Smax + KB - 1) / KB;  // >= one block per split
-    for (int n = 1; n <= max_ns && n <= MAX_SPLITS; ++n) {
-      const int rounds = (base * n + slots - 1) / slots;
-      const int blocks = (Smax + n * KB - 1) / (n * KB);
-      const double t = rounds * (fixed_blocks + blocks) + (n > 1 ? per_split * n : 0.0);
-      if (t < best * 0.999) {
-        best = t;
-        ns = n;
-      }
-    }
+    const int max_ns = (Smax + KB - 1) / KB;
+    ns = slots / (base > 0 ? base : 1);
+    if (ns > max_ns) ns = max_ns;
+    if (ns < 1) ns = 1;
   }
   if (ns > MAX_SPLITS) ns = MAX_SPLITS;
   int chunk = (Smax + ns - 1) / ns;
