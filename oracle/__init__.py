@@ -25,6 +25,7 @@ Modules:
   accept     greedy and rejection-sampling acceptance          (P1, rejection sampling; P3 2, 5; P4 1.3)
   step       the four stages composed
   commit     KV rollback / compaction after acceptance; greedy decoding (P3 5; P4 1.3)
+  dense_heads  the heads on every tree row (M = B*T) and each head's top-k (P1, heads; sketch code)
 
 Every function has at least one pin in ``tests/test_oracle_*.py`` that ties it
 to something other than itself (worked examples printed on the pages, closed
