@@ -156,6 +156,44 @@ int medusa_heads(const void* hidden, const void* w1, int64_t w1_head_stride,
                  medusa_dtype_t dt, float* logits, void* ws, size_t ws_bytes,
                  hipStream_t stream);
 
+/* Dense variant: the heads on the hidden state of every tree token (M = B*T
+ * rows), each head's top-k kept instead of its logits.
+ *
+ * P1, section "Medusa의 핵심 철학 ... 잔차 블록": the same residual block and
+ * vocab projection as medusa_heads; P1, section "소스코드 레벨 구조 분석"
+ * (generate_candidates): head d keeps its k_d largest logits.  Running the
+ * heads on all tree rows gives the next step's candidates at whichever node
+ * is accepted.
+ *
+ *   hidden    [M][H]        dt
+ *   w1, wlm   as medusa_heads (wlm_head_stride 0 = one shared projection)
+ *   tree      supplies K (= tree K) and k_d (its per-depth top-k, kmax the
+ *             largest)
+ *   topk_idx  [M][K][kmax] int32: row m, head d: the k_d vocab indices with
+ *             the largest logits, largest first, equal logits by lower
+ *             index; entries k_d..kmax-1 are -1
+ *   topk_val  [M][K][kmax] fp32 or NULL: the matching logits (0 in padding)
+ *   logits    [M][K][V] fp32 or NULL: also write every logit (the top-k is
+ *             the same either way)
+ * bf16: tiled MFMA GEMMs; the vocab projection's epilogue reduces each
+ * 128-column tile to its top-kmax, and a second kernel merges the tiles, so
+ * the logits never reach HBM unless asked for.  The ranking is decided on
+ * the fp32 logits the kernel computes (fp32 accumulation of bf16 products,
+ * the residual output rounded to bf16).  f32: plain VALU products.
+ * Constraints: K == tree K; V >= kmax; bf16: H % 128 == 0, V % 4 == 0,
+ * strides multiples of 8; pointers 16-byte aligned.
+ * Workspace: the residual output of every head and the per-tile candidates
+ * (bf16), or r and the logits (f32); no initialisation needed.
+ */
+size_t medusa_heads_dense_workspace_size(int M, int H, int V, int K, const medusa_tree_t* tree,
+                                         medusa_dtype_t dt);
+
+int medusa_heads_dense(const void* hidden, const void* w1, int64_t w1_head_stride,
+                       const void* wlm, int64_t wlm_head_stride, int M, int H, int V, int K,
+                       const medusa_tree_t* tree, medusa_dtype_t dt, int32_t* topk_idx,
+                       float* topk_val, float* logits, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Stage 3+4: per-head top-k and candidate tree tokens
  *

@@ -158,6 +158,30 @@ def tree_candidates(head_logits: torch.Tensor, root: torch.Tensor, ctx_len: torc
     return topk_idx, tree_tokens, pos
 
 
+def heads_dense(hidden: torch.Tensor, w1: torch.Tensor, wlm: torch.Tensor, tree: "Tree",
+                values: bool = True, logits=None, outs=None, ws=None, stream=None):
+    """Dense-variant heads: hidden [M,H]; w1 [K,H,H]; wlm [K,V,H] or [V,H]
+    (shared) -> (topk_idx [M,K,kmax] int32, topk_val [M,K,kmax] fp32 or None).
+    ``logits`` (a [M,K,V] fp32 tensor) also receives every logit."""
+    lib = _lib.load()
+    M, H = hidden.shape
+    K = w1.shape[0]
+    shared = wlm.dim() == 2
+    V = wlm.shape[0] if shared else wlm.shape[1]
+    dt = _dt(hidden)
+    dev = hidden.device
+    if outs is None:
+        outs = (torch.empty((M, K, tree.kmax), dtype=torch.int32, device=dev),
+                torch.empty((M, K, tree.kmax), dtype=torch.float32, device=dev) if values else None)
+    idx, val = outs
+    nbytes = lib.medusa_heads_dense_workspace_size(M, H, V, K, tree.handle, dt)
+    ws, nb = _workspace(nbytes, dev, ws)
+    _check(lib.medusa_heads_dense(_ptr(hidden), _ptr(w1), H * H, _ptr(wlm), 0 if shared else V * H,
+                                  M, H, V, K, tree.handle, dt, _ptr(idx), _ptr(val), _ptr(logits),
+                                  _ptr(ws), nb, _stream(stream)))
+    return idx, val
+
+
 def tree_attention_workspace_size(B, Hq, Hkv, D, ctx_max, tree: Tree, dtype) -> int:
     return _lib.load().medusa_tree_attention_workspace_size(
         B, Hq, Hkv, D, ctx_max, tree.handle, F32 if dtype == torch.float32 else BF16)

@@ -1,0 +1,611 @@
+// Dense-variant Medusa heads: the K heads on the hidden state of every tree
+// token at once (M = B*T rows) as tiled MFMA GEMMs, with each head's top-k
+// taken from the vocab projection's output tiles.
+//
+// P1 ("Medusa 심층 아키텍처"), section "Medusa의 핵심 철학 ... 잔차 블록을 포함한
+// Medusa 헤드 구조": head k maps a hidden state h to r = SiLU(W1_k h) + h and
+// then to logits W_lm,k r; its section "소스코드 레벨 구조 분석" keeps every
+// head's top-k logits as that head's candidates.  Run on all B*T tree rows,
+// the heads leave the next step's candidates in place for whichever node is
+// accepted.
+//
+// bf16 design (gfx950)
+//   C[m][n] = sum_k X[m][k] W[n][k], X the activations [M][Kd] and W the
+//   weights [N][Kd], both k-contiguous.  v_mfma_f32_16x16x32_bf16 takes 16
+//   weight rows as A and 16 activation rows as B, so a lane's accumulator
+//   holds one activation row and 4 consecutive output columns.
+//   Workgroup: BM activation rows (64 or 128) x 128 output columns, 4 waves
+//   in a 2 x 2 arrangement of (BM/2) x 64 wave tiles, k-steps of 64.  Both
+//   tiles of a k-step go global -> registers two steps ahead (buffer loads
+//   whose descriptors end at the matrices' ends, every load issued
+//   unconditionally so each wait covers exactly its step) -> LDS (two
+//   buffers, one barrier per step).  LDS rows are 128 bytes, 16-byte chunk c
+//   of row r at 16 * (c ^ ((r >> 1) & 7)): the MFMA operand reads (lane group
+//   g of k-step s reads chunk 4s + g of its row) and the staging writes are
+//   free of bank conflicts under the gfx950 rule (16-byte reads in lane
+//   groups {0-3, 12-15, 20-27} and +32, 16-byte writes in groups of 8
+//   consecutive lanes).
+//   Workgroups are numbered so that the row tiles of one weight tile run on
+//   one XCD (dispatch gives workgroup i to XCD i % 8): the weight tile is
+//   read from HBM once and served to the others from that XCD's L2.
+//   Residual-block epilogue: bf16(SiLU(acc) + h).  Vocab-projection
+//   epilogue: the fp32 tile goes to LDS; each row's 128 columns are scanned
+//   in column order by 256/BM threads, each keeping a sorted list of its
+//   largest values (a value enters only if strictly larger, so equal logits
+//   keep the lower column first); the lists of a row are merged and the
+//   row's top-kmax (logit, column) pairs written as that tile's candidates.
+//   A second kernel merges every row's tile candidates into each head's
+//   top-k.  The fp32 logits reach HBM only when the caller asks for them.
+#include "internal.h"
+
+using namespace medusa;
+using namespace medusa::dev;
+
+namespace {
+
+constexpr int BN = 128;               // output columns per workgroup
+constexpr int BK = 64;                // k per step
+constexpr int TROW = BK * 2;          // bytes per staged row
+constexpr int RSRC_WORD3 = 0x00020000;
+
+enum { EPI_RESID = 1, EPI_TOPK = 2 };
+
+__device__ __forceinline__ int toff(int r, int c) { return r * TROW + 16 * (c ^ ((r >> 1) & 7)); }
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+struct DenseArgs {
+  const uint16_t* x;  // head h's activations: x + h * x_hstride, [M][Kd]
+  int64_t x_hstride;
+  const uint16_t* w;  // head h's weights: w + h * w_hstride, [N][Kd]
+  int64_t w_hstride;
+  int M, N, Kd;
+  int mtiles, ntiles, tasks, per_xcd;
+  // residual block
+  const uint16_t* hid;  // [M][Kd], N == Kd
+  uint16_t* r_out;      // [heads][M][N]
+  // vocab projection
+  int K;                // heads (for the [M][K][...] layouts)
+  int kmax;
+  float* cand_v;        // [M][K][ntiles][kmax]
+  int32_t* cand_i;
+  float* logits;        // optional [M][K][N]
+};
+
+// Sorted insertion into a KM-entry list (descending value, ties keep the
+// earlier entry first): the new pair enters at the first entry it strictly
+// exceeds and everything below moves down one place.
+template <int KM>
+__device__ __forceinline__ void list_insert(float (&tv)[KM], int (&ti)[KM], float x, int xi) {
+#pragma unroll
+  for (int s = 0; s < KM; ++s) {
+    const bool take = x > tv[s];
+    const float ov = tv[s];
+    const int oi = ti[s];
+    tv[s] = take ? x : ov;
+    ti[s] = take ? xi : oi;
+    x = take ? ov : x;
+    xi = take ? oi : xi;
+  }
+}
+
+template <int BM, int EPI, int KM>
+__global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
+  constexpr int MT = BM / 32;         // 16-row activation tiles per wave
+  constexpr int XCH = BM * 8 / 256;   // 16-byte X chunks per thread per step
+  constexpr int WCH = BN * 8 / 256;   // 16-byte W chunks per thread per step
+  constexpr int CH = XCH + WCH;
+  constexpr int XT = BM * TROW;       // X tile bytes (W tile follows)
+  constexpr int STAGE = (BM + BN) * TROW;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int id = blockIdx.x;
+  const int task = (id & 7) * a.per_xcd + (id >> 3);
+  if (task >= a.tasks) return;  // the whole workgroup leaves before any barrier
+  const int mt = task % a.mtiles;
+  const int rest = task / a.mtiles;
+  const int nt = rest % a.ntiles;
+  const int head = rest / a.ntiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  const uint16_t* xb = a.x + head * a.x_hstride + static_cast<int64_t>(m0) * a.Kd;
+  const uint16_t* wb = a.w + head * a.w_hstride + static_cast<int64_t>(n0) * a.Kd;
+  const int xrows = min(BM, a.M - m0), wrows = min(BN, a.N - n0);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xb), 0, xrows * a.Kd * 2, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wb), 0, wrows * a.Kd * 2, RSRC_WORD3);
+
+  // this thread's chunks c = tid + 256u of each tile: row c / 8, chunk c % 8
+  int goff[CH], loff[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const bool isx = u < XCH;
+    const int c = tid + 256 * (isx ? u : u - XCH);
+    goff[u] = (c >> 3) * a.Kd * 2 + (c & 7) * 16;
+    loff[u] = (isx ? 0 : XT) + toff(c >> 3, c & 7);
+  }
+  auto gload = [&](uint4 (&R)[CH], int ks) __attribute__((always_inline)) {
+    const int kb = ks * TROW;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) R[u] = bload16(u < XCH ? rx : rw, goff[u] + kb);
+  };
+  auto lput = [&](const uint4 (&R)[CH], char* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) *reinterpret_cast<uint4*>(st + loff[u]) = R[u];
+  };
+
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // operand rows: W wc*64 + 16j + l16, X wr*(BM/2) + 16i + l16; chunk 4s + g
+  const int sw = (l16 >> 1) & 7;
+  const int cx0 = 16 * (g ^ sw), cx1 = 16 * ((4 + g) ^ sw);
+  const int wrow = XT + (wc * 64 + l16) * TROW;
+  const int xrow = (wr * (BM / 2) + l16) * TROW;
+  auto compute = [&](const char* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int cx = s ? cx1 : cx0;
+      bf16x8 wf[4], xf[MT];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wf[j] = as_bf16x8(*reinterpret_cast<const uint4*>(st + wrow + j * 16 * TROW + cx));
+#pragma unroll
+      for (int i = 0; i < MT; ++i) xf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(st + xrow + i * 16 * TROW + cx));
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Pipeline: block b is in registers R[b & 1] until it is written to LDS
+  // buffer b & 1 during step b - 1; nk is even, so the unrolled pair of steps
+  // keeps every register index a constant.  Loads of blocks past the end
+  // read zeros or bytes of the next row and are never used.
+  const int nk = a.Kd / BK;
+  uint4 R[2][CH];
+  gload(R[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
+  gload(R[1], 1);
+  __builtin_amdgcn_sched_barrier(0);
+  lput(R[0], smem);
+  gload(R[0], 2);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ks += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      compute(smem + j * STAGE);
+      lput(R[(j + 1) & 1], smem + ((j + 1) & 1) * STAGE);
+      gload(R[(j + 1) & 1], ks + j + 3);
+      __syncthreads();
+    }
+  }
+
+  if constexpr (EPI == EPI_RESID) {
+    // r[head][m][n] = bf16(SiLU(acc) + h[m][n]), 4 consecutive n per lane
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = m0 + wr * (BM / 2) + 16 * i + l16;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wc * 64 + 16 * j + 4 * g;
+        if (n >= a.N) continue;  // N % 4 == 0: all 4 columns are in range
+        const uint2 hv = *reinterpret_cast<const uint2*>(a.hid + static_cast<int64_t>(m) * a.Kd + n);
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float y = acc[i][j][e];
+          const uint32_t hb = (e & 1) ? ((e < 2 ? hv.x : hv.y) >> 16) : ((e < 2 ? hv.x : hv.y) & 0xffffu);
+          o[e] = y / (1.0f + expf(-y)) + bf16_bits_to_f32(hb);
+        }
+        uint16_t* dst = a.r_out + (static_cast<int64_t>(head) * a.M + m) * a.N + n;
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2(f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
+                       f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16));
+      }
+    }
+  } else {
+    // the fp32 tile in LDS: column granule q (4 columns) of row r at
+    // r * 512 + 16 * (q ^ (r & 7)); the loop's last barrier freed the buffers
+    float* tile = reinterpret_cast<float*>(smem);
+    auto tgran = [](int r, int q) { return r * 128 + 4 * (q ^ (r & 7)); };  // in floats
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(tile + tgran(wr * (BM / 2) + 16 * i + l16, wc * 16 + 4 * j + g)) = acc[i][j];
+    __syncthreads();
+    if (a.logits) {  // rows of the tile to logits[m][head][n0 ..], 8 rows per pass
+#pragma unroll
+      for (int p = 0; p < BM / 8; ++p) {
+        const int r = p * 8 + (tid >> 5), q = tid & 31;
+        const int m = m0 + r, n = n0 + 4 * q;
+        if (m < a.M && n < a.N)
+          *reinterpret_cast<f32x4*>(a.logits + (static_cast<int64_t>(m) * a.K + head) * a.N + n) =
+              *reinterpret_cast<const f32x4*>(tile + tgran(r, q));
+      }
+    }
+    constexpr int TPR = 256 / BM;   // threads per row
+    constexpr int CPT = BN / TPR;   // columns per thread
+    const int r = tid / TPR, part = tid % TPR;
+    float tv[KM];
+    int ti[KM];
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {
+      tv[s] = -INFINITY;
+      ti[s] = 0x7fffffff;
+    }
+#pragma unroll 4
+    for (int q = 0; q < CPT / 4; ++q) {
+      const int qq = part * (CPT / 4) + q;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(tile + tgran(r, qq));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = n0 + 4 * qq + e;
+        if (v[e] > tv[KM - 1] && n < a.N) list_insert<KM>(tv, ti, v[e], n);
+      }
+    }
+    __syncthreads();  // every thread is done with the tile
+    // the row's other threads hand their lists over (each covers later
+    // columns than the one before it, so merging in order keeps ties right)
+    float* lv = tile;
+    int* li = reinterpret_cast<int*>(tile + 256 * KM);
+    if (part) {
+#pragma unroll
+      for (int s = 0; s < KM; ++s) {
+        lv[tid * KM + s] = tv[s];
+        li[tid * KM + s] = ti[s];
+      }
+    }
+    __syncthreads();
+    if (part == 0) {
+      for (int o = 1; o < TPR; ++o) {
+        for (int s = 0; s < KM; ++s) {
+          const float x = lv[(tid + o) * KM + s];
+          if (!(x > tv[KM - 1])) break;  // the list is sorted: nothing after it enters either
+          list_insert<KM>(tv, ti, x, li[(tid + o) * KM + s]);
+        }
+      }
+      const int m = m0 + r;
+      if (m < a.M) {
+        const int64_t base = ((static_cast<int64_t>(m) * a.K + head) * a.ntiles + nt) * a.kmax;
+#pragma unroll
+        for (int s = 0; s < KM; ++s) {
+          if (s < a.kmax) {
+            a.cand_v[base + s] = tv[s];
+            a.cand_i[base + s] = ti[s];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---- final merge: each (row, head) keeps its k_d best candidates ----------
+// One wave per (row m, head d).  Lanes take lists (tile candidates, sorted)
+// or strided elements of a logits row into their own sorted lists; then k_d
+// rounds of a wave-wide arg-max over the lanes' list heads (larger value, or
+// equal value and lower index) pop the winners in order.
+struct MergeArgs {
+  const float* v;      // LISTS: [M][K][nlist][kmax]; ROW: [M][K][N]
+  const int32_t* ix;   // LISTS only
+  int M, K, nlist, kmax, N;
+  const int32_t* kpd;  // [K] candidates kept by head d
+  int32_t* out_idx;    // [M][K][kmax_out]
+  float* out_val;      // optional, same layout
+  int kmax_out;
+};
+
+template <int KM, bool LISTS>
+__global__ __launch_bounds__(256) void dense_topk_merge(MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // = m * K + d
+  if (row >= a.M * a.K) return;  // whole wave: no barrier below
+  const int d = row % a.K;
+  float tv[KM];
+  int ti[KM];
+#pragma unroll
+  for (int s = 0; s < KM; ++s) {
+    tv[s] = -INFINITY;
+    ti[s] = 0x7fffffff;
+  }
+  if constexpr (LISTS) {
+    const float* v = a.v + static_cast<int64_t>(row) * a.nlist * a.kmax;
+    const int32_t* ix = a.ix + static_cast<int64_t>(row) * a.nlist * a.kmax;
+    for (int l = lane; l < a.nlist; l += 64) {
+      for (int s = 0; s < a.kmax; ++s) {
+        const float x = v[l * a.kmax + s];
+        if (!(x > tv[KM - 1])) break;
+        list_insert<KM>(tv, ti, x, ix[l * a.kmax + s]);
+      }
+    }
+  } else {
+    const float* v = a.v + static_cast<int64_t>(row) * a.N;
+    for (int n = lane; n < a.N; n += 64) {
+      const float x = v[n];
+      if (x > tv[KM - 1]) list_insert<KM>(tv, ti, x, n);
+    }
+  }
+  const int kd = a.kpd[d];
+  int32_t* oi = a.out_idx + static_cast<int64_t>(row) * a.kmax_out;
+  float* ov = a.out_val ? a.out_val + static_cast<int64_t>(row) * a.kmax_out : nullptr;
+  for (int s = 0; s < a.kmax_out; ++s) {
+    float bv = tv[0];
+    int bi = ti[0];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ovv = __shfl_xor(bv, off);
+      const int oii = __shfl_xor(bi, off);
+      const bool take = ovv > bv || (ovv == bv && oii < bi);
+      bv = take ? ovv : bv;
+      bi = take ? oii : bi;
+    }
+    if (s < kd) {
+      if (lane == 0) {
+        oi[s] = bi;
+        if (ov) ov[s] = bv;
+      }
+      // the lane holding the winner drops it from its list
+      if (ti[0] == bi && tv[0] == bv) {
+#pragma unroll
+        for (int q = 0; q + 1 < KM; ++q) {
+          tv[q] = tv[q + 1];
+          ti[q] = ti[q + 1];
+        }
+        tv[KM - 1] = -INFINITY;
+        ti[KM - 1] = 0x7fffffff;
+      }
+    } else if (lane == 0) {
+      oi[s] = -1;
+      if (ov) ov[s] = 0.f;
+    }
+  }
+}
+
+// ---- fp32: plain VALU products (small configurations) ---------------------
+struct DenseF32Args {
+  const float* x;  // [M][H] hidden, or r [K][M][H]
+  int64_t x_hstride;
+  const float* w;  // [K][N][H]
+  int64_t w_hstride;
+  int M, N, H, K;
+  const float* hid;  // residual: [M][H]
+  float* out;        // residual: r [K][M][N]; logits: [M][K][N]
+  bool resid;
+};
+
+__global__ __launch_bounds__(256) void dense_f32(DenseF32Args a) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.K) * a.M * a.N;
+  if (t >= total) return;
+  const int n = static_cast<int>(t % a.N);
+  const int m = static_cast<int>((t / a.N) % a.M);
+  const int h = static_cast<int>(t / (static_cast<int64_t>(a.N) * a.M));
+  const float* x = a.x + h * a.x_hstride + static_cast<int64_t>(m) * a.H;
+  const float* w = a.w + h * a.w_hstride + static_cast<int64_t>(n) * a.H;
+  float acc = 0.f;
+  for (int k = 0; k < a.H; ++k) acc = fmaf(w[k], x[k], acc);
+  if (a.resid) {
+    a.out[(static_cast<int64_t>(h) * a.M + m) * a.N + n] =
+        acc / (1.0f + expf(-acc)) + a.hid[static_cast<int64_t>(m) * a.H + n];
+  } else {
+    a.out[(static_cast<int64_t>(m) * a.K + h) * a.N + n] = acc;
+  }
+}
+
+// ---- host -------------------------------------------------------------------
+int km_for(int kmax) { return kmax <= 4 ? 4 : kmax <= 8 ? 8 : kmax <= 12 ? 12 : kmax <= 16 ? 16 : 32; }
+
+struct DensePlan {
+  int BM, mtiles, ntiles, KM;
+  size_t r_bytes, cand_off, cand_v_bytes, cand_i_off, ws_bytes;
+};
+
+DensePlan dense_plan(int M, int H, int V, int K, int kmax, medusa_dtype_t dt) {
+  DensePlan p{};
+  p.KM = km_for(kmax);
+  if (dt == MEDUSA_BF16) {
+    p.BM = M <= 64 ? 64 : 128;
+    p.mtiles = (M + p.BM - 1) / p.BM;
+    p.ntiles = (V + BN - 1) / BN;
+    p.r_bytes = round_up(static_cast<size_t>(K) * M * H * 2, 256);
+    p.cand_off = p.r_bytes;
+    p.cand_v_bytes = round_up(static_cast<size_t>(M) * K * p.ntiles * kmax * 4, 256);
+    p.cand_i_off = p.cand_off + p.cand_v_bytes;
+    p.ws_bytes = p.cand_i_off + p.cand_v_bytes;
+  } else {
+    p.r_bytes = round_up(static_cast<size_t>(K) * M * H * 4, 256);
+    p.cand_off = p.r_bytes;  // logits [M][K][V] fp32
+    p.ws_bytes = p.cand_off + round_up(static_cast<size_t>(M) * K * V * 4, 256);
+  }
+  return p;
+}
+
+// LDS: the two staging buffers, then (vocab projection) the fp32 tile and
+// the per-thread candidate lists, each reusing the same bytes
+template <int BM, int EPI, int KM>
+constexpr int dense_lds() {
+  constexpr int stage = 2 * (BM + BN) * TROW;
+  constexpr int tile = EPI == EPI_TOPK ? BM * BN * 4 : 0;
+  constexpr int lists = EPI == EPI_TOPK ? 2 * 256 * KM * 4 : 0;
+  return stage > tile ? (stage > lists ? stage : lists) : (tile > lists ? tile : lists);
+}
+
+template <int BM, int EPI, int KM>
+int launch_gemm(const DenseArgs& a, hipStream_t s, const char* what) {
+  constexpr int lds = dense_lds<BM, EPI, KM>();
+  static_assert(lds <= 64 * 1024, "dense heads LDS above the default limit");
+  const int grid = 8 * a.per_xcd;
+  hipLaunchKernelGGL((dense_gemm_bf16<BM, EPI, KM>), dim3(grid), dim3(256), lds, s, a);
+  return check_launch(what);
+}
+
+template <int BM, int KM>
+int launch_topk_gemm(const DenseArgs& a, hipStream_t s) {
+  return launch_gemm<BM, EPI_TOPK, KM>(a, s, "dense heads vocab projection");
+}
+
+int launch_topk_bm(const DenseArgs& a, int BM, int KM, hipStream_t s) {
+#define MEDUSA_DENSE_KM(BMv)                                   \
+  switch (KM) {                                                \
+    case 4: return launch_topk_gemm<BMv, 4>(a, s);             \
+    case 8: return launch_topk_gemm<BMv, 8>(a, s);             \
+    case 12: return launch_topk_gemm<BMv, 12>(a, s);           \
+    case 16: return launch_topk_gemm<BMv, 16>(a, s);           \
+    default: return launch_topk_gemm<BMv, 32>(a, s);           \
+  }
+  if (BM == 64) {
+    MEDUSA_DENSE_KM(64)
+  }
+  MEDUSA_DENSE_KM(128)
+#undef MEDUSA_DENSE_KM
+}
+
+template <bool LISTS>
+int launch_merge(const MergeArgs& a, int KM, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(a.M) * a.K + 3) / 4));
+  switch (KM) {
+    case 4: hipLaunchKernelGGL((dense_topk_merge<4, LISTS>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((dense_topk_merge<8, LISTS>), grid, dim3(256), 0, s, a); break;
+    case 12: hipLaunchKernelGGL((dense_topk_merge<12, LISTS>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((dense_topk_merge<16, LISTS>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((dense_topk_merge<32, LISTS>), grid, dim3(256), 0, s, a); break;
+  }
+  return check_launch("dense heads top-k merge");
+}
+
+}  // namespace
+
+extern "C" size_t medusa_heads_dense_workspace_size(int M, int H, int V, int K,
+                                                    const medusa_tree_t* tree, medusa_dtype_t dt) {
+  if (!tree || M < 1 || H < 1 || V < 1 || K < 1) return 0;
+  if (dt != MEDUSA_F32 && dt != MEDUSA_BF16) return 0;
+  return dense_plan(M, H, V, K, tree->kmax, dt).ws_bytes;
+}
+
+extern "C" int medusa_heads_dense(const void* hidden, const void* w1, int64_t w1_head_stride,
+                                  const void* wlm, int64_t wlm_head_stride, int M, int H, int V,
+                                  int K, const medusa_tree_t* tree, medusa_dtype_t dt,
+                                  int32_t* topk_idx, float* topk_val, float* logits, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  int rc = check_tree(tree);
+  if (rc) return rc;
+  MEDUSA_CHECK_ARG(hidden && w1 && wlm && topk_idx, "hidden, w1, wlm and topk_idx must be non-NULL");
+  MEDUSA_CHECK_ARG(M >= 1 && H >= 1, "M=%d, H=%d must be >= 1", M, H);
+  MEDUSA_CHECK_ARG(K == tree->K, "K=%d must equal the tree's head count %d", K, tree->K);
+  MEDUSA_CHECK_ARG(V >= tree->kmax, "V=%d smaller than the largest top-k %d", V, tree->kmax);
+  MEDUSA_CHECK_ARG(dt == MEDUSA_F32 || dt == MEDUSA_BF16, "unknown dtype %d", static_cast<int>(dt));
+  MEDUSA_CHECK_ARG(K == 1 || w1_head_stride >= static_cast<int64_t>(H) * H,
+                   "w1_head_stride=%lld smaller than H*H", static_cast<long long>(w1_head_stride));
+  MEDUSA_CHECK_ARG(wlm_head_stride == 0 || wlm_head_stride >= static_cast<int64_t>(V) * H,
+                   "wlm_head_stride=%lld must be 0 (shared) or >= V*H",
+                   static_cast<long long>(wlm_head_stride));
+  MEDUSA_CHECK_ARG(aligned16(hidden) && aligned16(w1) && aligned16(wlm) && aligned16(topk_idx) &&
+                       aligned16(topk_val) && aligned16(logits),
+                   "pointers must be 16-byte aligned");
+  const DensePlan p = dense_plan(M, H, V, K, tree->kmax, dt);
+  if (!ws || ws_bytes < p.ws_bytes || !aligned256(ws)) {
+    set_error("dense heads workspace: need %zu bytes, 256-byte aligned (got %zu at %p)", p.ws_bytes,
+              ws_bytes, ws);
+    return MEDUSA_EWORKSPACE;
+  }
+  char* w = static_cast<char*>(ws);
+  MergeArgs mg{};
+  mg.M = M;
+  mg.K = K;
+  mg.kmax = tree->kmax;
+  mg.kpd = tree->d_kpd;
+  mg.out_idx = topk_idx;
+  mg.out_val = topk_val;
+  mg.kmax_out = tree->kmax;
+  if (dt == MEDUSA_F32) {
+    DenseF32Args f{};
+    f.x = static_cast<const float*>(hidden);
+    f.x_hstride = 0;
+    f.w = static_cast<const float*>(w1);
+    f.w_hstride = w1_head_stride;
+    f.M = M;
+    f.N = H;
+    f.H = H;
+    f.K = K;
+    f.hid = static_cast<const float*>(hidden);
+    f.out = reinterpret_cast<float*>(w);
+    f.resid = true;
+    int64_t total = static_cast<int64_t>(K) * M * H;
+    hipLaunchKernelGGL(dense_f32, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, stream, f);
+    if ((rc = check_launch("dense heads residual block (f32)"))) return rc;
+    float* lg = logits ? logits : reinterpret_cast<float*>(w + p.cand_off);
+    f.x = reinterpret_cast<const float*>(w);
+    f.x_hstride = static_cast<int64_t>(M) * H;
+    f.w = static_cast<const float*>(wlm);
+    f.w_hstride = wlm_head_stride;
+    f.N = V;
+    f.out = lg;
+    f.resid = false;
+    total = static_cast<int64_t>(K) * M * V;
+    hipLaunchKernelGGL(dense_f32, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, stream, f);
+    if ((rc = check_launch("dense heads vocab projection (f32)"))) return rc;
+    mg.v = lg;
+    mg.N = V;
+    return launch_merge<false>(mg, p.KM, stream);
+  }
+  MEDUSA_CHECK_ARG(H % 128 == 0, "bf16 dense heads need H %% 128 == 0 (H=%d)", H);
+  MEDUSA_CHECK_ARG(V % 4 == 0, "bf16 dense heads need V %% 4 == 0 (V=%d)", V);
+  MEDUSA_CHECK_ARG(w1_head_stride % 8 == 0 && wlm_head_stride % 8 == 0,
+                   "bf16 head strides must be multiples of 8 elements");
+  MEDUSA_CHECK_ARG(static_cast<int64_t>(BN) * H * 2 < (1ll << 31) && static_cast<int64_t>(p.BM) * H * 2 < (1ll << 31),
+                   "H=%d too large (tile byte offsets are 32-bit)", H);
+  DenseArgs a{};
+  a.M = M;
+  a.Kd = H;
+  a.K = K;
+  a.kmax = tree->kmax;
+  a.mtiles = p.mtiles;
+  // stage 1: r = bf16(SiLU(W1 h) + h) for every head, into the workspace
+  a.x = static_cast<const uint16_t*>(hidden);
+  a.x_hstride = 0;
+  a.w = static_cast<const uint16_t*>(w1);
+  a.w_hstride = w1_head_stride;
+  a.N = H;
+  a.ntiles = (H + BN - 1) / BN;
+  a.tasks = p.mtiles * a.ntiles * K;
+  a.per_xcd = (a.tasks + 7) / 8;
+  a.hid = static_cast<const uint16_t*>(hidden);
+  a.r_out = reinterpret_cast<uint16_t*>(w);
+  rc = p.BM == 64 ? launch_gemm<64, EPI_RESID, 4>(a, stream, "dense heads residual block")
+                  : launch_gemm<128, EPI_RESID, 4>(a, stream, "dense heads residual block");
+  if (rc) return rc;
+  // stage 2: logits tiles of every head and their per-tile top-kmax
+  DenseArgs b = a;
+  b.x = reinterpret_cast<const uint16_t*>(w);
+  b.x_hstride = static_cast<int64_t>(M) * H;
+  b.w = static_cast<const uint16_t*>(wlm);
+  b.w_hstride = wlm_head_stride;
+  b.N = V;
+  b.ntiles = p.ntiles;
+  b.tasks = p.mtiles * p.ntiles * K;
+  b.per_xcd = (b.tasks + 7) / 8;
+  b.cand_v = reinterpret_cast<float*>(w + p.cand_off);
+  b.cand_i = reinterpret_cast<int32_t*>(w + p.cand_i_off);
+  b.logits = logits;
+  rc = launch_topk_bm(b, p.BM, p.KM, stream);
+  if (rc) return rc;
+  mg.v = b.cand_v;
+  mg.ix = b.cand_i;
+  mg.nlist = p.ntiles;
+  return launch_merge<true>(mg, p.KM, stream);
+}
