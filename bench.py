@@ -165,6 +165,16 @@ def build_step(w, dev):
         api.tree_attention_layers(q_all, k_all, v_all, ctx, w.ctx, tree, out=out_all,
                                   ws=ws_attn_layers)
 
+    # dense variant of the heads (every tree row, M = B*T), a figure of its own
+    dense_rows = synth.normal((w.B * w.T, w.H), 1.0, synth.seed_for(w.cfg_id, synth.T_HIDDEN, 0, 1), dev,
+                              torch.bfloat16)
+    dense_idx = torch.empty((w.B * w.T, w.K, tree.kmax), dtype=torch.int32, device=dev)
+    dense_val = torch.empty((w.B * w.T, w.K, tree.kmax), dtype=torch.float32, device=dev)
+    ws_dense = ws(api._lib.load().medusa_heads_dense_workspace_size(w.B * w.T, w.H, w.V, w.K, tree.handle, 1))
+
+    def stage_heads_dense():
+        api.heads_dense(dense_rows, w1, wlm, tree, outs=(dense_idx, dense_val), ws=ws_dense)
+
     def stage_accept():
         for tau, o in acc_outs.items():
             api.accept_paths(base, logits, toks, tree, ua, us, tau, outs=o, ws=ws_acc)
@@ -185,7 +195,7 @@ def build_step(w, dev):
 
     keep = dict(hidden=hidden, w1=w1, wlm=wlm, tree=tree, layers=layers, base=base)
     return step, (stage_heads, stage_candidates, stage_attention, stage_accept, stage_commit,
-                  stage_attention_batched), keep
+                  stage_attention_batched, stage_heads_dense), keep
 
 
 def _capture(fn):
@@ -229,7 +239,7 @@ def time_gpu(w, args):
     step, stages, keep = build_step(w, dev)
     torch.cuda.synchronize()
     (stage_heads, stage_candidates, stage_attention, stage_accept, stage_commit,
-     stage_attention_batched) = stages
+     stage_attention_batched, stage_heads_dense) = stages
 
     run = step if args.eager else _capture(step).replay
     log(f"warmup {args.warmup}, timing {args.steps} steps ({'eager' if args.eager else 'graph'})")
@@ -256,7 +266,8 @@ def time_gpu(w, args):
     graphs = {"heads": _capture(stage_heads), "candidates": _capture(stage_candidates),
               "attention": _capture(all_layers), "accept": _capture(stage_accept),
               "commit": _capture(stage_commit),
-              "attention_batched": _capture(stage_attention_batched)}
+              "attention_batched": _capture(stage_attention_batched),
+              "heads_dense": _capture(stage_heads_dense)}
     reps = max(5, args.steps)
     stages_us = {n: 1000.0 * _time_replays(g.replay, reps, 3) for n, g in graphs.items()}
     attn_call_us = stages_us["attention"] / w.L
@@ -391,6 +402,16 @@ def main():
             "us_per_layer": round(stages_us["attention_batched"] / w.L, 2),
             "hbm_gbs": round(a_bytes * w.L / (stages_us["attention_batched"] * 1e-6) / 1e9, 1),
             "hbm_frac": round(a_bytes * w.L / (stages_us["attention_batched"] * 1e-6) / 1e9
+                              / HBM_PEAK_GBS, 4)},
+        "heads_dense": {
+            "rows": w.B * w.T,
+            "us": round(stages_us["heads_dense"], 2),
+            "mfma_tflops": round(heads_flops(w) * w.T / (stages_us["heads_dense"] * 1e-6) / 1e12, 1),
+            "mfma_frac": round(heads_flops(w) * w.T / (stages_us["heads_dense"] * 1e-6) / 1e12
+                               / BF16_MFMA_PEAK_TFLOPS, 4),
+            # weights read once dominate its bytes (the logits never leave the chip)
+            "hbm_gbs": round(w.K * (w.H * w.H + w.H * w.V) * 2 / (stages_us["heads_dense"] * 1e-6) / 1e9, 1),
+            "hbm_frac": round(w.K * (w.H * w.H + w.H * w.V) * 2 / (stages_us["heads_dense"] * 1e-6) / 1e9
                               / HBM_PEAK_GBS, 4)},
         "stages_us": {k: round(v, 2) for k, v in stages_us.items()},
         "wall_s_timed": round(wall_s, 4),

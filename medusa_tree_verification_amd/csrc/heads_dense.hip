@@ -294,6 +294,230 @@ __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
   }
 }
 
+// ---- large-M tiles: 256 x 256, direct-to-LDS loads -----------------------
+// For M > 128 (e.g. zephyr7b-shaped, M = 512) a workgroup of 8 waves takes
+// 256 activation rows x 256 output columns (wave tile 64 x 128), halving the
+// L2 -> LDS bytes per FLOP of the 128 x 128 tile.  Each 32-wide k-step's two
+// tiles (64-byte rows, chunk c of row r at 16 * (c ^ 2 * bit2(r))) are
+// written straight into LDS by buffer loads (`buffer_load_dwordx4 ... lds`:
+// lane i of a wave's load lands at the wave's LDS base + 16 i, so each lane
+// fetches the chunk that belongs at its position) into a ring of four stage
+// buffers, three steps ahead.  Each step: wait for this wave's loads of the
+// step and its own LDS reads of the previous one, one barrier, issue the
+// loads three steps ahead into the buffer everybody finished reading, then
+// the MFMAs.  The four buffers are separate LDS objects so that the
+// compiler's wait for the loads into one does not cover the others.
+constexpr int B2M = 256, B2N = 256, B2K = 32;
+constexpr int B2ROW = B2K * 2;               // 64 bytes per staged row
+constexpr int B2X = B2M * B2ROW;             // X tile bytes; the W tile follows
+constexpr int B2STAGE = (B2M + B2N) * B2ROW; // 32 KiB
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int b2swz(int r) { return ((r >> 2) & 1) << 1; }
+
+template <int EPI, int KM>
+__global__ __launch_bounds__(512) void dense_gemm_big(DenseArgs a) {
+  __shared__ __attribute__((aligned(16))) char st0[B2STAGE], st1[B2STAGE], st2[B2STAGE], st3[B2STAGE];
+  const int id = blockIdx.x;
+  const int task = (id & 7) * a.per_xcd + (id >> 3);
+  if (task >= a.tasks) return;  // the whole workgroup leaves before any barrier
+  const int mt = task % a.mtiles;
+  const int rest = task / a.mtiles;
+  const int nt = rest % a.ntiles;
+  const int head = rest / a.ntiles;
+  const int m0 = mt * B2M, n0 = nt * B2N;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;  // 64-row quarter, 128-column half
+  const int l16 = lane & 15, g = lane >> 4;
+
+  const uint16_t* xb = a.x + head * a.x_hstride + static_cast<int64_t>(m0) * a.Kd;
+  const uint16_t* wb = a.w + head * a.w_hstride + static_cast<int64_t>(n0) * a.Kd;
+  const int xrows = min(B2M, a.M - m0), wrows = min(B2N, a.N - n0);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xb), 0, xrows * a.Kd * 2, RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wb), 0, wrows * a.Kd * 2, RSRC_WORD3);
+
+  // this wave's loads: 16-row blocks 2*wave and 2*wave + 1 of each tile;
+  // lane i fills row i/4 of the block at position i%4 with chunk
+  // (i%4) ^ swizzle(row).  Rows past the matrices' ends are left as they
+  // are: they only feed outputs that are never written.
+  int goff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * (2 * wave + q) + (lane >> 2);
+    goff[q] = row * a.Kd * 2 + 16 * ((lane & 3) ^ b2swz(row));
+  }
+  auto dma = [&](char* st, int ks) __attribute__((always_inline)) {
+    const int kb = ks * B2ROW;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(st + (2 * wave + q) * 1024), 16, goff[q] + kb, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(st + B2X + (2 * wave + q) * 1024), 16, goff[q] + kb, 0, 0, 0);
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int cx = 16 * (g ^ b2swz(l16));
+  const int xrow = (wm * 64 + l16) * B2ROW + cx;
+  const int wrow = B2X + (wn * 128 + l16) * B2ROW + cx;
+  auto compute = [&](const char* st) __attribute__((always_inline)) {
+    bf16x8 xf[4], wf[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(st + xrow + i * 16 * B2ROW));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wf[j] = as_bf16x8(*reinterpret_cast<const uint4*>(st + wrow + j * 16 * B2ROW));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+  };
+  // s_waitcnt vmcnt(8) lgkmcnt(0) (expcnt untouched): this wave's loads of
+  // the current step are in (the two later steps' 8 loads may still fly) and
+  // its reads of the previous step's buffer are done
+  auto step = [&](char* cur, char* nxt, int ks) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0078);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    dma(nxt, ks + 3);  // past the end: bytes of the next row or zeros, never read
+    compute(cur);
+  };
+  const int nk = a.Kd / B2K;  // a multiple of 4
+  dma(st0, 0);
+  dma(st1, 1);
+  dma(st2, 2);
+  for (int ks = 0; ks < nk; ks += 4) {
+    step(st0, st3, ks);
+    step(st1, st0, ks + 1);
+    step(st2, st1, ks + 2);
+    step(st3, st2, ks + 3);
+  }
+  // every load (also those past the end) has landed before LDS is reused
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __syncthreads();
+
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 64 + 16 * i + l16;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = n0 + wn * 128 + 16 * j + 4 * g;
+        if (n >= a.N) continue;
+        const uint2 hv = *reinterpret_cast<const uint2*>(a.hid + static_cast<int64_t>(m) * a.Kd + n);
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float y = acc[i][j][e];
+          const uint32_t hw = e < 2 ? hv.x : hv.y;
+          o[e] = y / (1.0f + expf(-y)) + bf16_bits_to_f32((e & 1) ? (hw >> 16) : (hw & 0xffffu));
+        }
+        uint16_t* dst = a.r_out + (static_cast<int64_t>(head) * a.M + m) * a.N + n;
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2(f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
+                       f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16));
+      }
+    }
+  } else {
+    // two passes of 128 rows; rows 32a .. 32a + 31 of a pass sit in stage
+    // buffer a, column granule q (4 columns) of local row r at
+    // (r % 32) * 1024 + 16 * (q ^ (r & 7))
+    auto cell = [&](int r, int q) __attribute__((always_inline)) {
+      const int b = r >> 5;
+      char* base = b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3;
+      return reinterpret_cast<float*>(base + (r & 31) * 1024 + 16 * (q ^ (r & 7)));
+    };
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if ((wm >> 1) == pass) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<f32x4*>(cell((wm & 1) * 64 + 16 * i + l16, wn * 32 + 4 * j + g)) = acc[i][j];
+      }
+      __syncthreads();
+      if (a.logits) {  // 4 rows per pass of the 512 threads
+        for (int rr = 0; rr < 128; rr += 8) {
+          const int r = rr + (tid >> 6), q = tid & 63;
+          const int m = m0 + pass * 128 + r, n = n0 + 4 * q;
+          if (m < a.M && n < a.N)
+            *reinterpret_cast<f32x4*>(a.logits + (static_cast<int64_t>(m) * a.K + head) * a.N + n) =
+                *reinterpret_cast<const f32x4*>(cell(r, q));
+        }
+      }
+      // 4 adjacent lanes per row, 64 columns each
+      const int r = tid >> 2, part = tid & 3;
+      float tv[KM];
+      int ti[KM];
+#pragma unroll
+      for (int s2 = 0; s2 < KM; ++s2) {
+        tv[s2] = -INFINITY;
+        ti[s2] = 0x7fffffff;
+      }
+#pragma unroll 4
+      for (int q = 0; q < 16; ++q) {
+        const int qq = part * 16 + q;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(cell(r, qq));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = n0 + 4 * qq + e;
+          if (v[e] > tv[KM - 1] && n < a.N) list_insert<KM>(tv, ti, v[e], n);
+        }
+      }
+      // merge with the lanes of the same row (xor 1, then xor 2): the list
+      // of the lower part goes first, so equal logits keep the lower column
+#pragma unroll
+      for (int sh = 1; sh <= 2; sh <<= 1) {
+        float pv[KM];
+        int pi[KM];
+#pragma unroll
+        for (int s2 = 0; s2 < KM; ++s2) {
+          pv[s2] = __shfl_xor(tv[s2], sh);
+          pi[s2] = __shfl_xor(ti[s2], sh);
+        }
+        if (part & sh) {  // this lane holds the later columns: start from the partner's list
+#pragma unroll
+          for (int s2 = 0; s2 < KM; ++s2) {
+            const float t0 = tv[s2];
+            const int i0 = ti[s2];
+            tv[s2] = pv[s2];
+            ti[s2] = pi[s2];
+            pv[s2] = t0;
+            pi[s2] = i0;
+          }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < KM; ++s2) {
+          if (pv[s2] > tv[KM - 1]) list_insert<KM>(tv, ti, pv[s2], pi[s2]);
+        }
+      }
+      const int m = m0 + pass * 128 + r;
+      if (part == 0 && m < a.M) {
+        const int64_t base = ((static_cast<int64_t>(m) * a.K + head) * a.ntiles + nt) * a.kmax;
+#pragma unroll
+        for (int s2 = 0; s2 < KM; ++s2) {
+          if (s2 < a.kmax) {
+            a.cand_v[base + s2] = tv[s2];
+            a.cand_i[base + s2] = ti[s2];
+          }
+        }
+      }
+      __syncthreads();  // the next pass rewrites the buffers
+    }
+  }
+}
+
 // ---- final merge: each (row, head) keeps its k_d best candidates ----------
 // One wave per (row m, head d).  Lanes take lists (tile candidates, sorted)
 // or strided elements of a logits row into their own sorted lists; then k_d
@@ -411,6 +635,7 @@ int km_for(int kmax) { return kmax <= 4 ? 4 : kmax <= 8 ? 8 : kmax <= 12 ? 12 : 
 
 struct DensePlan {
   int BM, mtiles, ntiles, KM;
+  bool big;  // 256 x 256 tiles with direct-to-LDS loads
   size_t r_bytes, cand_off, cand_v_bytes, cand_i_off, ws_bytes;
 };
 
@@ -418,9 +643,13 @@ DensePlan dense_plan(int M, int H, int V, int K, int kmax, medusa_dtype_t dt) {
   DensePlan p{};
   p.KM = km_for(kmax);
   if (dt == MEDUSA_BF16) {
-    p.BM = M <= 64 ? 64 : 128;
+    // 256 x 256 tiles for large M; their epilogue keeps the accumulators of
+    // the second row half live while the first is ranked, which leaves room
+    // for lists of up to 12 entries without spilling
+    p.big = M > 128 && p.KM <= 12;
+    p.BM = p.big ? B2M : M <= 64 ? 64 : 128;
     p.mtiles = (M + p.BM - 1) / p.BM;
-    p.ntiles = (V + BN - 1) / BN;
+    p.ntiles = (V + (p.big ? B2N : BN) - 1) / (p.big ? B2N : BN);
     p.r_bytes = round_up(static_cast<size_t>(K) * M * H * 2, 256);
     p.cand_off = p.r_bytes;
     p.cand_v_bytes = round_up(static_cast<size_t>(M) * K * p.ntiles * kmax * 4, 256);
@@ -472,6 +701,21 @@ int launch_topk_bm(const DenseArgs& a, int BM, int KM, hipStream_t s) {
   }
   MEDUSA_DENSE_KM(128)
 #undef MEDUSA_DENSE_KM
+}
+
+template <int EPI, int KM>
+int launch_big(const DenseArgs& a, hipStream_t s, const char* what) {
+  hipLaunchKernelGGL((dense_gemm_big<EPI, KM>), dim3(8 * a.per_xcd), dim3(512), 0, s, a);
+  return check_launch(what);
+}
+
+int launch_topk_big(const DenseArgs& a, int KM, hipStream_t s) {
+  const char* what = "dense heads vocab projection (256 x 256 tiles)";
+  switch (KM) {  // the plan keeps KM <= 12 here
+    case 4: return launch_big<EPI_TOPK, 4>(a, s, what);
+    case 8: return launch_big<EPI_TOPK, 8>(a, s, what);
+    default: return launch_big<EPI_TOPK, 12>(a, s, what);
+  }
 }
 
 template <bool LISTS>
@@ -581,13 +825,14 @@ extern "C" int medusa_heads_dense(const void* hidden, const void* w1, int64_t w1
   a.w = static_cast<const uint16_t*>(w1);
   a.w_hstride = w1_head_stride;
   a.N = H;
-  a.ntiles = (H + BN - 1) / BN;
+  a.ntiles = (H + (p.big ? B2N : BN) - 1) / (p.big ? B2N : BN);
   a.tasks = p.mtiles * a.ntiles * K;
   a.per_xcd = (a.tasks + 7) / 8;
   a.hid = static_cast<const uint16_t*>(hidden);
   a.r_out = reinterpret_cast<uint16_t*>(w);
-  rc = p.BM == 64 ? launch_gemm<64, EPI_RESID, 4>(a, stream, "dense heads residual block")
-                  : launch_gemm<128, EPI_RESID, 4>(a, stream, "dense heads residual block");
+  if (p.big) rc = launch_big<EPI_RESID, 4>(a, stream, "dense heads residual block (256 x 256 tiles)");
+  else if (p.BM == 64) rc = launch_gemm<64, EPI_RESID, 4>(a, stream, "dense heads residual block");
+  else rc = launch_gemm<128, EPI_RESID, 4>(a, stream, "dense heads residual block");
   if (rc) return rc;
   // stage 2: logits tiles of every head and their per-tile top-kmax
   DenseArgs b = a;
@@ -602,7 +847,7 @@ extern "C" int medusa_heads_dense(const void* hidden, const void* w1, int64_t w1
   b.cand_v = reinterpret_cast<float*>(w + p.cand_off);
   b.cand_i = reinterpret_cast<int32_t*>(w + p.cand_i_off);
   b.logits = logits;
-  rc = launch_topk_bm(b, p.BM, p.KM, stream);
+  rc = p.big ? launch_topk_big(b, p.KM, stream) : launch_topk_bm(b, p.BM, p.KM, stream);
   if (rc) return rc;
   mg.v = b.cand_v;
   mg.ix = b.cand_i;
