@@ -164,12 +164,17 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
   const int l16 = lane & 15;
   const int grp = lane >> 4;
 
-  int ctx = a.ctx[b];
-  ctx = ctx < 0 ? 0 : (ctx > a.S_cap - a.T ? a.S_cap - a.T : ctx);
-  const int S = ctx + a.T;
   const int k_begin = split * a.chunk;
-  const int k_end = (split == a.NS - 1) ? S : min(S, k_begin + a.chunk);
-  const int nblk = k_end > k_begin ? (k_end - k_begin + KB - 1) / KB : 0;
+  // the sequence's bounds; each role reads ctx_len only after issuing its
+  // first loads, which do not depend on it
+  int ctx = 0, k_end = 0, nblk = 0;
+  auto read_ctx = [&]() __attribute__((always_inline)) {
+    ctx = a.ctx[b];
+    ctx = ctx < 0 ? 0 : (ctx > a.S_cap - a.T ? a.S_cap - a.T : ctx);
+    const int S = ctx + a.T;
+    k_end = (split == a.NS - 1) ? S : min(S, k_begin + a.chunk);
+    nblk = k_end > k_begin ? (k_end - k_begin + KB - 1) / KB : 0;
+  };
 
   // ---- staging roles: waves 8-9 load K rows, waves 10-11 V ----
   const bool k_role = wave < 10;
@@ -177,6 +182,7 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
   const uint16_t* gbase =
       (k_role ? a.k : a.v) + layer * a.kv_lstride + static_cast<int64_t>(bh) * a.S_cap * D;
   int goff[8];   // byte offsets of this thread's 8 loads within a block
+  int krow0;     // key of load 0 within its block (load i: krow0 + kstep * i, V: see below)
   int lds_w;     // this thread's LDS store offset within a slot (K: even loads)
   int lds_w_odd; // K: odd loads (their row is 8 further, which flips bit 3 of the swizzle)
   if (k_role) {
@@ -185,6 +191,7 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
     const int base = r * GROWB + c * 16;
 #pragma unroll
     for (int i = 0; i < 8; ++i) goff[i] = base + 8 * i * GROWB;
+    krow0 = r;
     lds_w = kq_off(r, c);
     lds_w_odd = kq_off(r + 8, c) - 8 * KROWB;
   } else {
@@ -194,21 +201,38 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
     const int base = (h * 32 + 4 * g) * GROWB + o * 16;
 #pragma unroll
     for (int i = 0; i < 8; ++i) goff[i] = base + (i < 4 ? i : 12 + i) * GROWB;
+    krow0 = h * 32 + 4 * g;
     lds_w = K_TILE + 8 * o * VROWB + 16 * ((h * 4 + g) ^ rot3(o & 7));
     lds_w_odd = 0;
   }
-  // a block's loads through a buffer resource that ends at the split's end:
-  // reads of keys >= k_end return zeros (never the unused cache slots)
+  // A block's loads go through a buffer resource that ends where the split
+  // can end at most (the next split's start, or the cache's end), a bound
+  // that does not depend on the context length: the first loads leave before
+  // ctx_len has arrived.  Rows of keys >= k_end (unused cache slots) are
+  // zeroed before they reach LDS, so nothing past the sequence can enter the
+  // products; keys past the bound read as zeros.
+  const int spec_end = (split == a.NS - 1) ? a.S_cap : min(a.S_cap, k_begin + a.chunk);
   auto gload = [&](uint4 (&x)[8], int blk) __attribute__((always_inline)) {
     const int kb = k_begin + blk * KB;
-    const int nrec = (k_end - kb) * GROWB;
+    const int nrec = (spec_end - kb) * GROWB;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(gbase + static_cast<int64_t>(kb) * D), 0, nrec > 0 ? nrec : 0,
         RSRC_WORD3);
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = bload16(r, goff[i]);
   };
-  auto lds_put = [&](const uint4 (&x)[8], char* slot) __attribute__((always_inline)) {
+  auto lds_put = [&](const uint4 (&xin)[8], char* slot, int blk) __attribute__((always_inline)) {
+    uint4 x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = xin[i];
+    const int lim = k_end - (k_begin + blk * KB);  // keys of this block below k_end
+    if (lim < KB) {  // the block reaches past the sequence (or the split)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = krow0 + (k_role ? 8 * i : (i < 4 ? i : 12 + i));
+        if (key >= lim) x[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
     if (k_role) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -248,14 +272,15 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
       gload(R[j], j);
       __builtin_amdgcn_sched_barrier(0);  // keep the blocks' loads in order
     }
-    if (nblk > 0) lds_put(R[0], ring);
+    read_ctx();
+    if (nblk > 0) lds_put(R[0], ring, 0);
     gload(R[0], NREG);
     __syncthreads();
     int ws = 1;  // slot of block blk + j + 1
     for (int blk = 0; blk < nblk; blk += NREG) {
 #pragma unroll
       for (int j = 0; j < NREG; ++j) {
-        if (blk + j + 1 < nblk) lds_put(R[(j + 1) % NREG], ring + ws * BLK_BYTES);
+        if (blk + j + 1 < nblk) lds_put(R[(j + 1) % NREG], ring + ws * BLK_BYTES, blk + j + 1);
         ws = ws == NSLOT - 1 ? 0 : ws + 1;
         gload(R[(j + 1) % NREG], blk + j + 1 + NREG);
         __syncthreads();
@@ -298,6 +323,8 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
       if (tid + 512 * u < nmask) smask[tid + 512 * u] = mv;
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  read_ctx();
   const uint32_t* smask32 = reinterpret_cast<const uint32_t*>(smask);
 
   // compute-wave state: this wave's query tiles qw, qw + 4, ...
