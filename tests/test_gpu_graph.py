@@ -73,3 +73,80 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for a, b in zip(snapshot(), ref):
             assert torch.equal(a, b), f"eager step after replay {rep} differs"
+
+
+def test_graph_replays_of_the_other_calls():
+    """All-layers attention, dense heads on both tile shapes (64 and 256
+    rows) and the commit of an accepted path, captured together; the caches
+    the commit edits in place are restored eagerly before every replay."""
+    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(L=3, ctx=600, H=256, V=3000, cfg_id=310)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    tree = api.Tree(parent, rank, w.topk)
+    per = [synth.attention_inputs(w, l, DEV)[:3] for l in range(w.L)]
+    q_all = torch.stack([p[0] for p in per])
+    k_all = torch.stack([p[1] for p in per])
+    v_all = torch.stack([p[2] for p in per])
+    ctx = torch.full((w.B,), w.ctx, dtype=torch.int32, device=DEV)
+    out_all = torch.empty_like(q_all)
+    _, w1, wlm = synth.head_inputs(w, DEV)
+    rows64 = synth.normal((64, w.H), 1.0, 11, DEV, torch.bfloat16)
+    rows256 = synth.normal((256, w.H), 1.0, 12, DEV, torch.bfloat16)
+    d64 = (torch.empty((64, w.K, tree.kmax), dtype=torch.int32, device=DEV),
+           torch.empty((64, w.K, tree.kmax), dtype=torch.float32, device=DEV))
+    d256 = (torch.empty((256, w.K, tree.kmax), dtype=torch.int32, device=DEV),
+            torch.empty((256, w.K, tree.kmax), dtype=torch.float32, device=DEV))
+    z = lambda n: torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
+    lib = api._lib.load()
+    ws_l = z(api.tree_attention_layers_workspace_size(w.L, w.B, w.Hq, w.Hkv, w.D, w.ctx, tree, torch.bfloat16))
+    ws_d64 = z(lib.medusa_heads_dense_workspace_size(64, w.H, w.V, w.K, tree.handle, 1))
+    ws_d256 = z(lib.medusa_heads_dense_workspace_size(256, w.H, w.V, w.K, tree.handle, 1))
+    # an accepted path of length 2 along the tree: root -> first child -> its first child
+    kids = [n for n in range(w.T) if parent[n] == 0]
+    grand = [n for n in range(w.T) if parent[n] == kids[0]]
+    nodes = torch.tensor([[0, kids[0], grand[0]] + [-1] * (w.K - 2)], dtype=torch.int32, device=DEV)
+    toks = torch.tensor([[5, 6, 7] + [-1] * (w.K - 2)], dtype=torch.int32, device=DEV)
+    alen = torch.tensor([2], dtype=torch.int32, device=DEV)
+    kc0, vc0 = k_all.clone(), v_all.clone()
+    kc, vc = k_all.clone(), v_all.clone()
+    ctx_next = torch.empty_like(ctx)
+    root_next = torch.empty_like(ctx)
+
+    def step():
+        api.tree_attention_layers(q_all, k_all, v_all, ctx, w.ctx, tree, out=out_all, ws=ws_l)
+        api.heads_dense(rows64, w1, wlm, tree, outs=d64, ws=ws_d64)
+        api.heads_dense(rows256, w1, wlm, tree, outs=d256, ws=ws_d256)
+        api.commit_accepted(kc, vc, alen, nodes, toks, ctx, tree, ctx_next, root_next)
+
+    outs = [out_all, *d64, *d256, kc, vc, ctx_next, root_next]
+
+    def restore():
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+
+    announce("graph 2: eager reference")
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in outs]
+    restore()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    restore()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    announce("graph 2: capture")
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for x in outs[:5] + outs[7:]:
+            x.zero_()                       # eager work between replays
+        restore()
+        torch.cuda.synchronize()
+        announce("graph 2: replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs from eager"
