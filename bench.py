@@ -149,13 +149,14 @@ def build_step(w, dev):
     ws_attn = ws(api.tree_attention_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.ctx, tree, torch.bfloat16))
     ws_attn_layers = ws(api.tree_attention_layers_workspace_size(w.L, w.B, w.Hq, w.Hkv, w.D, w.ctx,
                                                                  tree, torch.bfloat16))
+    ws_cand = ws(api.tree_candidates_workspace_size(w.B, w.V, tree))
     ws_acc = ws(max(api.accept_workspace_size(w.B, w.V, tree, t) for t in w.temperature))
 
     def stage_heads():
         api.heads(hidden, w1, wlm, logits=logits, ws=ws_heads)
 
     def stage_candidates():
-        api.tree_candidates(logits, root, ctx, tree, topk, toks, pos)
+        api.tree_candidates(logits, root, ctx, tree, topk, toks, pos, ws=ws_cand)
 
     def stage_attention(l):
         q, k, v = layers[l]

@@ -209,11 +209,16 @@ int medusa_heads_dense(const void* hidden, const void* w1, int64_t w1_head_strid
  *   topk_idx    [B][K][kmax] int32 (output; -1 beyond head d's k_d)
  *   tree_tokens [B][T] int32 (output)
  *   pos         [B][T] int32 (output)
+ * Workspace: each 512-column chunk's sorted top-kmax (logit, index) list
+ * per row, merged by a second kernel on the same stream; no initialisation
+ * needed, calls that share a workspace must not overlap.
  * ------------------------------------------------------------------------ */
+size_t medusa_tree_candidates_workspace_size(int B, int V, const medusa_tree_t* tree);
+
 int medusa_tree_candidates(const float* head_logits, const int32_t* root,
                            const int32_t* ctx_len, const medusa_tree_t* tree, int B, int V,
-                           int32_t* topk_idx, int32_t* tree_tokens, int32_t* pos,
-                           hipStream_t stream);
+                           int32_t* topk_idx, int32_t* tree_tokens, int32_t* pos, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Stage 5: tree-masked attention (one layer)

@@ -33,8 +33,9 @@ SIGNATURES = {
     "medusa_heads_dense": (c_int, [P_void, P_void, c_int64, P_void, c_int64, c_int, c_int, c_int,
                                    c_int, c_void_p, c_int, P_void, P_void, P_void, P_void,
                                    c_size_t, P_void]),
+    "medusa_tree_candidates_workspace_size": (c_size_t, [c_int, c_int, c_void_p]),
     "medusa_tree_candidates": (c_int, [P_void, P_void, P_void, c_void_p, c_int, c_int, P_void,
-                                       P_void, P_void, P_void]),
+                                       P_void, P_void, P_void, c_size_t, P_void]),
     "medusa_tree_attention_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int,
                                                         c_void_p, c_int]),
     "medusa_tree_attention": (c_int, [P_void, P_void, P_void, P_void, c_int, c_void_p, c_int,

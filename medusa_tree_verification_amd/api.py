@@ -140,8 +140,12 @@ def heads(hidden: torch.Tensor, w1: torch.Tensor, wlm: torch.Tensor, logits=None
     return logits
 
 
+def tree_candidates_workspace_size(B, V, tree: Tree) -> int:
+    return _lib.load().medusa_tree_candidates_workspace_size(B, V, tree.handle)
+
+
 def tree_candidates(head_logits: torch.Tensor, root: torch.Tensor, ctx_len: torch.Tensor,
-                    tree: Tree, topk_idx=None, tree_tokens=None, pos=None, stream=None):
+                    tree: Tree, topk_idx=None, tree_tokens=None, pos=None, ws=None, stream=None):
     """head_logits [B,K,V] fp32 -> (topk_idx [B,K,kmax], tree_tokens [B,T], pos [B,T]) int32."""
     lib = _lib.load()
     B, K, V = head_logits.shape
@@ -152,8 +156,9 @@ def tree_candidates(head_logits: torch.Tensor, root: torch.Tensor, ctx_len: torc
         tree_tokens = torch.empty((B, tree.T), dtype=torch.int32, device=dev)
     if pos is None:
         pos = torch.empty((B, tree.T), dtype=torch.int32, device=dev)
+    ws, nb = _workspace(lib.medusa_tree_candidates_workspace_size(B, V, tree.handle), dev, ws)
     _check(lib.medusa_tree_candidates(_ptr(head_logits), _ptr(root), _ptr(ctx_len), tree.handle, B,
-                                      V, _ptr(topk_idx), _ptr(tree_tokens), _ptr(pos),
+                                      V, _ptr(topk_idx), _ptr(tree_tokens), _ptr(pos), _ptr(ws), nb,
                                       _stream(stream)))
     return topk_idx, tree_tokens, pos
 

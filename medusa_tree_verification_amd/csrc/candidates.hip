@@ -11,215 +11,187 @@
 // equal).  Comparing (value, index) pairs this way is a total order, so the
 // result is unique and bit-exact.
 //
-// One workgroup of 1024 threads per (head, sequence), radix select:
-//   1. each logit becomes an order-preserving 32-bit key (larger logit ->
-//      larger key; -0 is keyed as +0);
-//   2. the k-th largest key K* is found digit by digit (11, 11 and 10 bits):
-//      an LDS histogram of the keys that match the digits found so far, then
-//      a scan from the top bucket down finds the bucket holding the k-th;
-//   3. every key above K* is a winner; when more keys equal K* than are still
-//      needed, the smallest indices among them are found the same way (a
-//      radix select on the index);
-//   4. the k winners are ranked by (value, index) inside one wave.
-// The same workgroup then writes the tree tokens and positions of the nodes
-// at depth head+1 (and the root, for head 0).
+// Two kernels spread every logit row over many CUs:
+//   1. one wave per (sequence, head, chunk of CW columns): each lane keeps a
+//      sorted list of its largest values, taking its columns in increasing
+//      order (a value enters only if strictly larger, so an equal logit of a
+//      later column stays behind); the chunk's top-kmax is then popped from
+//      the 64 lane lists by kmax wave-wide arg-max rounds and written as a
+//      sorted (logit, column) list;
+//   2. one wave per (sequence, head): the chunk lists (in column order) go
+//      into per-lane lists the same way, k_d arg-max rounds pop the head's
+//      candidates, and the same wave writes them, the tree tokens of the
+//      nodes at depth head+1, and (head 0) the root and every position.
+// The chunk lists live in the caller's workspace.
 #include "internal.h"
 
 using namespace medusa;
+using namespace medusa::dev;
 
 namespace {
 
-constexpr int THREADS = 1024;
-constexpr int WAVES = THREADS / 64;
-constexpr int REG_VALUES = 32;  // values per thread kept in registers
-constexpr int BINS = 2048;      // histogram buckets (11-bit digits)
-
-__device__ __forceinline__ uint32_t order_key(float y) {
-  uint32_t u = __float_as_uint(y == 0.f ? 0.f : y);  // -0 keyed as +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+constexpr int CW = 512;  // columns per chunk (8 per lane)
 
 struct CandArgs {
   const float* logits;  // [B][K][V]
-  int K, V, kmax, T;
+  int K, V, kmax, T, nchunks;
   const int32_t* kpd;    // [K]
   const int32_t* depth;  // [T]
   const int32_t* rank;   // [T]
   const int32_t* root;   // [B]
   const int32_t* ctx;    // [B]
+  float* cv;             // [B][K][nchunks][kmax] chunk lists
+  int32_t* ci;
   int32_t* topk;         // [B][K][kmax]
   int32_t* tree_tokens;  // [B][T]
   int32_t* pos;          // [B][T]
+  int rows;              // B * K
 };
 
-struct Shared {
-  int hist[BINS];
-  int wave_sum[WAVES];
-  int found_bin, found_before;  // bucket of the target rank, count above it
-  int n_win;
-  uint32_t win_key[MEDUSA_MAX_TOPK];
-  uint32_t win_idx[MEDUSA_MAX_TOPK];
-  int top[MEDUSA_MAX_TOPK];
-};
-
-// Given the histogram of one digit, find the bucket that holds the element
-// of rank `want` (1-based) counting from the top bucket (descending = true)
-// or from the bottom one.  Writes found_bin / found_before.
-__device__ void find_bucket(Shared& sh, int want, bool descending) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // thread t owns ordered positions 2t and 2t+1
-  const int b0 = descending ? BINS - 1 - 2 * tid : 2 * tid;
-  const int b1 = descending ? b0 - 1 : b0 + 1;
-  const int h0 = sh.hist[b0], h1 = sh.hist[b1];
-  int x = h0 + h1;  // inclusive scan over threads in position order
+// wave-wide arg-max of (value, index) pairs: larger value, then lower index
+__device__ __forceinline__ void wave_best(float& bv, int& bi) {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    const bool take = ov > bv || (ov == bv && oi < bi);
+    bv = take ? ov : bv;
+    bi = take ? oi : bi;
   }
-  if (lane == 63) sh.wave_sum[wave] = x;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += sh.wave_sum[w];
-  const int incl = before + x;
-  const int excl = incl - h0 - h1;
-  if (excl < want && want <= incl) {
-    if (want <= excl + h0) {
-      sh.found_bin = b0;
-      sh.found_before = excl;
-    } else {
-      sh.found_bin = b1;
-      sh.found_before = excl + h0;
-    }
-  }
-  __syncthreads();
 }
 
-template <bool REG>
-__global__ __launch_bounds__(THREADS) void topk_tree_kernel(CandArgs a) {
-  const int head = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const float* x = a.logits + (static_cast<int64_t>(b) * a.K + head) * a.V;
-  const int kd = a.kpd[head];
-  __shared__ Shared sh;
-
-  // ---- 1. keys ----
-  uint32_t keys[REG ? REG_VALUES : 1];
-  if (REG) {
+// the lane holding the popped winner drops it from its list
+template <int KM>
+__device__ __forceinline__ void list_pop_if(float (&tv)[KM], int (&ti)[KM], float bv, int bi) {
+  if (tv[0] == bv && ti[0] == bi) {
 #pragma unroll
-    for (int j = 0; j < REG_VALUES; ++j) {
-      const int v = tid + j * THREADS;
-      keys[j] = v < a.V ? order_key(x[v]) : 0u;  // key 0 is below every logit's key
+    for (int q = 0; q + 1 < KM; ++q) {
+      tv[q] = tv[q + 1];
+      ti[q] = ti[q + 1];
     }
+    tv[KM - 1] = -INFINITY;
+    ti[KM - 1] = 0x7fffffff;
   }
-  // visit every (key, index) of the row (registers or a strided re-read)
-  auto for_each = [&](auto&& f) __attribute__((always_inline)) {
-    if (REG) {
+}
+
+template <int KM>
+__device__ __forceinline__ void list_init(float (&tv)[KM], int (&ti)[KM]) {
 #pragma unroll
-      for (int j = 0; j < REG_VALUES; ++j) {
-        const int v = tid + j * THREADS;
-        if (v < a.V) f(keys[j], static_cast<uint32_t>(v));
-      }
-    } else {
-      for (int v = tid; v < a.V; v += THREADS) f(order_key(x[v]), static_cast<uint32_t>(v));
-    }
-  };
-
-  // ---- 2. K* = the kd-th largest key, one digit at a time ----
-  uint32_t prefix = 0, pmask = 0;
-  int want = kd;  // rank of K* among the keys matching the prefix
-  const int shifts[3] = {21, 10, 0};
-  const uint32_t widths[3] = {0x7FFu, 0x7FFu, 0x3FFu};
-  for (int p = 0; p < 3; ++p) {
-    for (int i = tid; i < BINS; i += THREADS) sh.hist[i] = 0;
-    __syncthreads();
-    for_each([&](uint32_t k, uint32_t) {
-      if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shifts[p]) & widths[p]], 1);
-    });
-    __syncthreads();
-    find_bucket(sh, want, true);
-    want -= sh.found_before;
-    prefix |= static_cast<uint32_t>(sh.found_bin) << shifts[p];
-    pmask |= widths[p] << shifts[p];
-    __syncthreads();  // everyone has read found_* before the next pass rewrites it
+  for (int s = 0; s < KM; ++s) {
+    tv[s] = -INFINITY;
+    ti[s] = 0x7fffffff;
   }
-  const uint32_t kstar = prefix;
-  const int equal = sh.hist[kstar & 0x3FFu];  // keys equal to K* (last digit's bucket)
-  // keys above K*: kd - want of them; ties needed: want (1 <= want <= equal)
+}
 
-  // ---- 3. winners: keys above K*, then the `want` smallest tied indices ----
-  uint32_t imax = 0xFFFFFFFFu;  // take tied indices <= imax
-  if (want < equal) {
-    // radix select of the want-th smallest index among keys == K* (2 digits)
-    uint32_t ip = 0, im = 0;
-    int w2 = want;
-    const int ishift[2] = {11, 0};
-    for (int p = 0; p < 2; ++p) {
-      __syncthreads();
-      for (int i = tid; i < BINS; i += THREADS) sh.hist[i] = 0;
-      __syncthreads();
-      for_each([&](uint32_t k, uint32_t v) {
-        if (k == kstar && (v & im) == ip) atomicAdd(&sh.hist[(v >> ishift[p]) & 0x7FFu], 1);
-      });
-      __syncthreads();
-      find_bucket(sh, w2, false);
-      w2 -= sh.found_before;
-      ip |= static_cast<uint32_t>(sh.found_bin) << ishift[p];
-      im |= 0x7FFu << ishift[p];
-    }
-    imax = ip;
+template <int KM>
+__global__ __launch_bounds__(256) void cand_chunks(CandArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // = row * nchunks + chunk
+  if (w >= a.rows * a.nchunks) return;                // whole wave, no barrier
+  const int row = w / a.nchunks, chunk = w % a.nchunks;
+  const float* x = a.logits + static_cast<int64_t>(row) * a.V;
+  const int c0 = chunk * CW;
+  float v[CW / 64];
+#pragma unroll
+  for (int i = 0; i < CW / 64; ++i) {  // every load in flight before any compare
+    const int c = c0 + 64 * i + lane;
+    v[i] = c < a.V ? x[c] : -INFINITY;
   }
-  if (tid == 0) sh.n_win = 0;
-  __syncthreads();
-  for_each([&](uint32_t k, uint32_t v) {
-    if (k > kstar || (k == kstar && v <= imax)) {
-      const int slot = atomicAdd(&sh.n_win, 1);
-      if (slot < MEDUSA_MAX_TOPK) {
-        sh.win_key[slot] = k;
-        sh.win_idx[slot] = v;
-      }
-    }
-  });
-  __syncthreads();
-
-  // ---- 4. rank the kd winners by (value desc, index asc) ----
-  if (tid < kd) {
-    const uint32_t k = sh.win_key[tid], v = sh.win_idx[tid];
-    int r = 0;
-    for (int j = 0; j < kd; ++j) {
-      const uint32_t kj = sh.win_key[j], vj = sh.win_idx[j];
-      r += (kj > k || (kj == k && vj < v)) ? 1 : 0;
-    }
-    sh.top[r] = static_cast<int>(v);
+  float tv[KM];
+  int ti[KM];
+  list_init<KM>(tv, ti);
+#pragma unroll
+  for (int i = 0; i < CW / 64; ++i) {
+    const int c = c0 + 64 * i + lane;
+    if (v[i] > tv[KM - 1] && c < a.V) list_insert<KM>(tv, ti, v[i], c);
   }
-  __syncthreads();
+  const int64_t base = (static_cast<int64_t>(row) * a.nchunks + chunk) * a.kmax;
+  for (int s = 0; s < a.kmax; ++s) {
+    float bv = tv[0];
+    int bi = ti[0];
+    wave_best(bv, bi);
+    if (lane == 0) {
+      a.cv[base + s] = bv;
+      a.ci[base + s] = bi;
+    }
+    list_pop_if<KM>(tv, ti, bv, bi);
+  }
+}
 
-  int32_t* out = a.topk + (static_cast<int64_t>(b) * a.K + head) * a.kmax;
-  for (int j = tid; j < a.kmax; j += THREADS) out[j] = j < kd ? sh.top[j] : -1;
-
-  // tree tokens of the nodes this head feeds
-  const int c = a.ctx[b];
-  for (int n = tid; n < a.T; n += THREADS) {
-    const int d = a.depth[n];
-    if (n == 0) {
-      if (head == 0) {
-        a.tree_tokens[static_cast<int64_t>(b) * a.T] = a.root[b];
-        a.pos[static_cast<int64_t>(b) * a.T] = c;
-      }
-    } else if (d == head + 1) {
-      a.tree_tokens[static_cast<int64_t>(b) * a.T + n] = sh.top[a.rank[n]];
-      a.pos[static_cast<int64_t>(b) * a.T + n] = c + d;
+template <int KM>
+__global__ __launch_bounds__(256) void cand_merge_tree(CandArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // = b * K + d
+  if (row >= a.rows) return;                              // whole wave, no barrier
+  const int b = row / a.K, d = row % a.K;
+  float tv[KM];
+  int ti[KM];
+  list_init<KM>(tv, ti);
+  const float* cv = a.cv + static_cast<int64_t>(row) * a.nchunks * a.kmax;
+  const int32_t* ci = a.ci + static_cast<int64_t>(row) * a.nchunks * a.kmax;
+  for (int l = lane; l < a.nchunks; l += 64) {
+    for (int s = 0; s < a.kmax; ++s) {
+      const float x = cv[l * a.kmax + s];
+      if (!(x > tv[KM - 1])) break;  // a sorted list: nothing after it enters either
+      list_insert<KM>(tv, ti, x, ci[l * a.kmax + s]);
     }
   }
+  const int kd = a.kpd[d];
+  int32_t* out = a.topk + static_cast<int64_t>(row) * a.kmax;
+  int32_t* tok = a.tree_tokens + static_cast<int64_t>(b) * a.T;
+  for (int s = 0; s < a.kmax; ++s) {
+    if (s < kd) {
+      float bv = tv[0];
+      int bi = ti[0];
+      wave_best(bv, bi);
+      if (lane == 0) out[s] = bi;
+      // nodes at depth d+1 with rank s carry this candidate
+      for (int n = lane; n < a.T; n += 64)
+        if (a.depth[n] == d + 1 && a.rank[n] == s) tok[n] = bi;
+      list_pop_if<KM>(tv, ti, bv, bi);
+    } else if (lane == 0) {
+      out[s] = -1;
+    }
+  }
+  if (d == 0) {
+    const int c = a.ctx[b];
+    for (int n = lane; n < a.T; n += 64) {
+      a.pos[static_cast<int64_t>(b) * a.T + n] = c + a.depth[n];
+      if (n == 0) tok[0] = a.root[b];
+    }
+  }
+}
+
+int km_for(int kmax) { return kmax <= 4 ? 4 : kmax <= 8 ? 8 : kmax <= 12 ? 12 : kmax <= 16 ? 16 : 32; }
+
+size_t cand_ws_bytes(int B, int V, const medusa_tree_t* tree, int* nchunks) {
+  const int nc = (V + CW - 1) / CW;
+  if (nchunks) *nchunks = nc;
+  const size_t one = round_up(static_cast<size_t>(B) * tree->K * nc * tree->kmax * 4, 256);
+  return 2 * one;
+}
+
+template <int KM>
+int launch_cand(const CandArgs& a, hipStream_t s) {
+  const int64_t chunks = static_cast<int64_t>(a.rows) * a.nchunks;
+  hipLaunchKernelGGL(cand_chunks<KM>, dim3(static_cast<unsigned>((chunks + 3) / 4)), dim3(256), 0, s, a);
+  int rc = check_launch("top-k chunks");
+  if (rc) return rc;
+  hipLaunchKernelGGL(cand_merge_tree<KM>, dim3(static_cast<unsigned>((a.rows + 3) / 4)), dim3(256), 0, s, a);
+  return check_launch("top-k merge / tree tokens");
 }
 
 }  // namespace
 
+extern "C" size_t medusa_tree_candidates_workspace_size(int B, int V, const medusa_tree_t* tree) {
+  if (!tree || B < 1 || V < 1) return 0;
+  return cand_ws_bytes(B, V, tree, nullptr);
+}
+
 extern "C" int medusa_tree_candidates(const float* head_logits, const int32_t* root,
                                       const int32_t* ctx_len, const medusa_tree_t* tree, int B,
                                       int V, int32_t* topk_idx, int32_t* tree_tokens, int32_t* pos,
-                                      hipStream_t stream) {
+                                      void* ws, size_t ws_bytes, hipStream_t stream) {
   clear_error();
   int rc = check_tree(tree);
   if (rc) return rc;
@@ -229,9 +201,13 @@ extern "C" int medusa_tree_candidates(const float* head_logits, const int32_t* r
   for (int d = 0; d < tree->K; ++d)
     MEDUSA_CHECK_ARG(tree->kpd[d] <= V, "head %d keeps %d candidates but V=%d", d + 1,
                      tree->kpd[d], V);
-  // indices are radix-selected in two 11-bit digits
-  MEDUSA_CHECK_ARG(V <= (1 << 22), "V=%d above 4194304", V);
+  MEDUSA_CHECK_ARG(static_cast<int64_t>(B) * tree->K * V < (1ll << 31), "B*K*V too large");
   CandArgs a{};
+  const size_t need = cand_ws_bytes(B, V, tree, &a.nchunks);
+  if (!ws || ws_bytes < need || !aligned256(ws)) {
+    set_error("candidates workspace: need %zu bytes, 256-byte aligned (got %zu at %p)", need, ws_bytes, ws);
+    return MEDUSA_EWORKSPACE;
+  }
   a.logits = head_logits;
   a.K = tree->K;
   a.V = V;
@@ -242,13 +218,17 @@ extern "C" int medusa_tree_candidates(const float* head_logits, const int32_t* r
   a.rank = tree->d_rank;
   a.root = root;
   a.ctx = ctx_len;
+  a.cv = static_cast<float*>(ws);
+  a.ci = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2);
   a.topk = topk_idx;
   a.tree_tokens = tree_tokens;
   a.pos = pos;
-  dim3 grid(tree->K, B);
-  if (V <= THREADS * REG_VALUES)
-    hipLaunchKernelGGL(topk_tree_kernel<true>, grid, dim3(THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(topk_tree_kernel<false>, grid, dim3(THREADS), 0, stream, a);
-  return check_launch("top-k / tree tokens");
+  a.rows = B * tree->K;
+  switch (km_for(tree->kmax)) {
+    case 4: return launch_cand<4>(a, stream);
+    case 8: return launch_cand<8>(a, stream);
+    case 12: return launch_cand<12>(a, stream);
+    case 16: return launch_cand<16>(a, stream);
+    default: return launch_cand<32>(a, stream);
+  }
 }

@@ -74,23 +74,6 @@ struct DenseArgs {
   float* logits;        // optional [M][K][N]
 };
 
-// Sorted insertion into a KM-entry list (descending value, ties keep the
-// earlier entry first): the new pair enters at the first entry it strictly
-// exceeds and everything below moves down one place.
-template <int KM>
-__device__ __forceinline__ void list_insert(float (&tv)[KM], int (&ti)[KM], float x, int xi) {
-#pragma unroll
-  for (int s = 0; s < KM; ++s) {
-    const bool take = x > tv[s];
-    const float ov = tv[s];
-    const int oi = ti[s];
-    tv[s] = take ? x : ov;
-    ti[s] = take ? xi : oi;
-    x = take ? ov : x;
-    xi = take ? oi : xi;
-  }
-}
-
 template <int BM, int EPI, int KM>
 __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
   constexpr int MT = BM / 32;         // 16-row activation tiles per wave

@@ -91,5 +91,26 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Sorted insertion into a KM-entry list (descending value; an entry enters
+// only at a place whose value it strictly exceeds, so among equal values the
+// one inserted first stays first, and -0 equals +0): the new pair takes the
+// first place it beats and every entry from there on moves down exactly one
+// place (a displaced entry is not compared again: it may equal the next one).
+template <int KM>
+__device__ __forceinline__ void list_insert(float (&tv)[KM], int (&ti)[KM], float x, int xi) {
+  bool shifting = false;
+#pragma unroll
+  for (int s = 0; s < KM; ++s) {
+    const bool take = shifting || x > tv[s];
+    shifting = take;
+    const float ov = tv[s];
+    const int oi = ti[s];
+    tv[s] = take ? x : ov;
+    ti[s] = take ? xi : oi;
+    x = take ? ov : x;
+    xi = take ? oi : xi;
+  }
+}
+
 }  // namespace dev
 }  // namespace medusa

@@ -83,7 +83,7 @@ def test_candidates_deterministic():
 
 @pytest.mark.parametrize("V", [40000, 131072])
 def test_candidates_large_vocab(V):
-    """Vocabularies past 32768 entries re-read the row on every pass."""
+    """Vocabularies of many chunks per row (up to 256 chunk lists merged)."""
     kpd = (10, 5)
     parent, rank = synth.cartesian_tree(kpd)
     g = torch.Generator(device=DEV).manual_seed(V)

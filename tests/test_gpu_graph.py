@@ -35,10 +35,11 @@ def test_graph_replays_match_eager():
     ws_h = z(api.heads_workspace_size(w.B, w.H, w.K, torch.bfloat16))
     ws_a = z(api.tree_attention_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.ctx, tree, torch.bfloat16))
     ws_c = z(api.accept_workspace_size(w.B, w.V, tree, 0.0))
+    ws_t = z(api.tree_candidates_workspace_size(w.B, w.V, tree))
 
     def step():
         api.heads(hidden, w1, wlm, logits=logits, ws=ws_h)
-        api.tree_candidates(logits, root, ctx, tree, topk, toks, pos)
+        api.tree_candidates(logits, root, ctx, tree, topk, toks, pos, ws=ws_t)
         for l, (q, k, v) in enumerate(layers):
             api.tree_attention(q, k, v, ctx, w.ctx, tree, out=outs[l], ws=ws_a)
         api.accept_paths(base, None, toks, tree, None, None, 0.0, outs=acc, ws=ws_c)

@@ -152,3 +152,21 @@ def test_dense_argument_errors():
                                 8, 128, 256, 2, t.handle, api.BF16, idx.data_ptr(), None, None,
                                 ws.data_ptr(), ws.numel(), None)
     assert rc == api.EWORKSPACE
+
+
+@pytest.mark.parametrize("M", [64, 256])
+def test_dense_heavy_ties(M):
+    """Head 0's projection is zero (every logit exactly 0: the lowest indices
+    win); head 1's vocab rows repeat with period 7 (every logit has exact
+    duplicates).  Both tile shapes (M = 64 and M = 256)."""
+    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=1, H=128, V=1024, K=2, topk=(10, 10), T=12,
+                                                  cfg_id=450 + M)
+    hidden, w1, wlm = synth.head_inputs(w, DEV, M=M)
+    wlm[0].zero_()
+    wlm[1] = wlm[1][torch.arange(1024, device=DEV) % 7]
+    t = _tree((10, 10), 12)
+    announce("dense heads heavy ties", M)
+    idx, _ = api.heads_dense(hidden, w1, wlm, t)
+    torch.cuda.synchronize()
+    assert (idx[:, 0].cpu().numpy() == np.arange(10)).all()
+    _check(hidden, w1, wlm, t, (10, 10), TOL_BF16, round_r=True)
