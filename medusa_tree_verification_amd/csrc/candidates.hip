@@ -48,15 +48,46 @@ struct CandArgs {
   int rows;              // B * K
 };
 
-// wave-wide arg-max of (value, index) pairs: larger value, then lower index
+// Wave-wide arg-max of (value, index) pairs (larger value, then lower index),
+// left in every lane.  All on the vector ALU: DPP quad permutes pair lanes
+// that differ in bit 0 and bit 1, the half-row and row mirrors then pair
+// uniform groups of 4 and 8, and the 16- and 32-lane swaps finish across rows.
+__device__ __forceinline__ void best_of(float& bv, int& bi, float ov, int oi) {
+  const bool take = ov > bv || (ov == bv && oi < bi);
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void best_dpp(float& bv, int& bi) {
+  const float ov = __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(bv), CTRL, 0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xf, 0xf, false);
+  best_of(bv, bi, ov, oi);
+}
+
 __device__ __forceinline__ void wave_best(float& bv, int& bi) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    const bool take = ov > bv || (ov == bv && oi < bi);
-    bv = take ? ov : bv;
-    bi = take ? oi : bi;
+  best_dpp<0xB1>(bv, bi);   // quad_perm [1,0,3,2]
+  best_dpp<0x4E>(bv, bi);   // quad_perm [2,3,0,1]
+  best_dpp<0x141>(bv, bi);  // row_half_mirror
+  best_dpp<0x140>(bv, bi);  // row_mirror
+  {
+    // rows 0<->1 and 2<->3: both halves of the swap carry one candidate each
+    const auto v = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto i = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(bi), static_cast<unsigned>(bi), false, false);
+    float av = __uint_as_float(v[0]);
+    int ai = static_cast<int>(i[0]);
+    best_of(av, ai, __uint_as_float(v[1]), static_cast<int>(i[1]));
+    bv = av;
+    bi = ai;
+  }
+  {
+    const auto v = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto i = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(bi), static_cast<unsigned>(bi), false, false);
+    float av = __uint_as_float(v[0]);
+    int ai = static_cast<int>(i[0]);
+    best_of(av, ai, __uint_as_float(v[1]), static_cast<int>(i[1]));
+    bv = av;
+    bi = ai;
   }
 }
 
@@ -124,34 +155,46 @@ __global__ __launch_bounds__(256) void cand_merge_tree(CandArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // = b * K + d
   if (row >= a.rows) return;                              // whole wave, no barrier
   const int b = row / a.K, d = row % a.K;
+  // the first 64 nodes' depth and rank are loaded now and used after the pops
+  const int dn0 = lane < a.T ? a.depth[lane] : -1;
+  const int rn0 = lane < a.T ? a.rank[lane] : 0;
+  const int kd = a.kpd[d];
   float tv[KM];
   int ti[KM];
   list_init<KM>(tv, ti);
   const float* cv = a.cv + static_cast<int64_t>(row) * a.nchunks * a.kmax;
   const int32_t* ci = a.ci + static_cast<int64_t>(row) * a.nchunks * a.kmax;
   for (int l = lane; l < a.nchunks; l += 64) {
-    for (int s = 0; s < a.kmax; ++s) {
-      const float x = cv[l * a.kmax + s];
-      if (!(x > tv[KM - 1])) break;  // a sorted list: nothing after it enters either
-      list_insert<KM>(tv, ti, x, ci[l * a.kmax + s]);
+    float xv[KM];
+    int xi[KM];
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {  // the whole chunk list in flight at once
+      xv[s] = s < a.kmax ? cv[l * a.kmax + s] : -INFINITY;
+      xi[s] = s < a.kmax ? ci[l * a.kmax + s] : 0x7fffffff;
     }
+    // a sorted list: once an entry stays out, every later one does too
+#pragma unroll
+    for (int s = 0; s < KM; ++s)
+      if (xv[s] > tv[KM - 1]) list_insert<KM>(tv, ti, xv[s], xi[s]);
   }
-  const int kd = a.kpd[d];
-  int32_t* out = a.topk + static_cast<int64_t>(row) * a.kmax;
+  // k_d arg-max rounds; lane s keeps the head's candidate of rank s
+  int mine = -1;
+  for (int s = 0; s < kd; ++s) {
+    float bv = tv[0];
+    int bi = ti[0];
+    wave_best(bv, bi);
+    mine = lane == s ? bi : mine;
+    list_pop_if<KM>(tv, ti, bv, bi);
+  }
+  if (lane < a.kmax) a.topk[static_cast<int64_t>(row) * a.kmax + lane] = mine;  // -1 past k_d
+  // nodes at depth d+1 carry the candidate of their rank
   int32_t* tok = a.tree_tokens + static_cast<int64_t>(b) * a.T;
-  for (int s = 0; s < a.kmax; ++s) {
-    if (s < kd) {
-      float bv = tv[0];
-      int bi = ti[0];
-      wave_best(bv, bi);
-      if (lane == 0) out[s] = bi;
-      // nodes at depth d+1 with rank s carry this candidate
-      for (int n = lane; n < a.T; n += 64)
-        if (a.depth[n] == d + 1 && a.rank[n] == s) tok[n] = bi;
-      list_pop_if<KM>(tv, ti, bv, bi);
-    } else if (lane == 0) {
-      out[s] = -1;
-    }
+  for (int n0 = 0; n0 < a.T; n0 += 64) {
+    const int n = n0 + lane;
+    const int dn = n0 == 0 ? dn0 : (n < a.T ? a.depth[n] : -1);
+    const int rn = n0 == 0 ? rn0 : (n < a.T ? a.rank[n] : 0);
+    const int t = __shfl(mine, dn == d + 1 ? rn : 0);
+    if (dn == d + 1) tok[n] = t;
   }
   if (d == 0) {
     const int c = a.ctx[b];
