@@ -439,8 +439,46 @@ __global__ __launch_bounds__(512) void dense_gemm_big(DenseArgs a) {
                 *reinterpret_cast<const f32x4*>(cell(r, q));
         }
       }
-      // 4 adjacent lanes per row, 64 columns each
+      // 4 adjacent lanes per row, 64 columns each.  The row's bound: each
+      // lane's c-th largest 8-column maximum (c = ceil(kmax / 4) <= 3), then
+      // the smallest over the row's 4 lanes.  At least 4c >= kmax values of
+      // the row reach it, so no value below it is among the row's kmax
+      // largest; only values at or above it go through the sorted insertion
+      // (most lanes hold a handful), taken in column order.
       const int r = tid >> 2, part = tid & 3;
+      float g1 = -INFINITY, g2 = -INFINITY, g3 = -INFINITY;  // largest granule maxima, descending
+#pragma unroll
+      for (int gi = 0; gi < 8; ++gi) {
+        const int qq = part * 16 + 2 * gi;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(cell(r, qq));
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(cell(r, qq + 1));
+        const int nb = n0 + 4 * qq;
+        float gm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gm = fmaxf(gm, nb + e < a.N ? v0[e] : -INFINITY);
+          gm = fmaxf(gm, nb + 4 + e < a.N ? v1[e] : -INFINITY);
+        }
+        const float t1 = fmaxf(g1, gm), r1 = fminf(g1, gm);
+        const float t2 = fmaxf(g2, r1), r2 = fminf(g2, r1);
+        g3 = fmaxf(g3, r2);
+        g2 = t2;
+        g1 = t1;
+      }
+      const int c = (a.kmax + 3) >> 2;
+      float th = c == 1 ? g1 : (c == 2 ? g2 : g3);
+      th = fminf(th, __shfl_xor(th, 1));
+      th = fminf(th, __shfl_xor(th, 2));
+      uint32_t cand[2] = {0u, 0u};  // bit 4q + e: column 4(part*16 + q) + e reaches the bound
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(cell(r, part * 16 + q));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = n0 + 4 * (part * 16 + q) + e;
+          if (v[e] >= th && n < a.N) cand[q >> 3] |= 1u << (4 * (q & 7) + e);
+        }
+      }
       float tv[KM];
       int ti[KM];
 #pragma unroll
@@ -448,14 +486,14 @@ __global__ __launch_bounds__(512) void dense_gemm_big(DenseArgs a) {
         tv[s2] = -INFINITY;
         ti[s2] = 0x7fffffff;
       }
-#pragma unroll 4
-      for (int q = 0; q < 16; ++q) {
-        const int qq = part * 16 + q;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(cell(r, qq));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int n = n0 + 4 * qq + e;
-          if (v[e] > tv[KM - 1] && n < a.N) list_insert<KM>(tv, ti, v[e], n);
+      while (__builtin_amdgcn_ballot_w64((cand[0] | cand[1]) != 0u)) {
+        if (cand[0] | cand[1]) {
+          const int i = cand[0] ? __builtin_ctz(cand[0]) : 32 + __builtin_ctz(cand[1]);
+          if (cand[0]) cand[0] &= cand[0] - 1u;
+          else cand[1] &= cand[1] - 1u;
+          const int qq = part * 16 + (i >> 2);
+          const float x = cell(r, qq)[i & 3];
+          if (x > tv[KM - 1]) list_insert<KM>(tv, ti, x, n0 + 4 * qq + (i & 3));
         }
       }
       // merge with the lanes of the same row (xor 1, then xor 2): the list
