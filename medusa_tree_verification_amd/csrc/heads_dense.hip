@@ -92,6 +92,7 @@ __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
   const int nt = rest % a.ntiles;
   const int head = rest / a.ntiles;
   const int m0 = mt * BM, n0 = nt * BN;
+  if (m0 >= a.M || n0 >= a.N) return;  // no tile past the matrices (whole workgroup, no barrier yet)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -309,6 +310,7 @@ __global__ __launch_bounds__(512) void dense_gemm_big(DenseArgs a) {
   const int nt = rest % a.ntiles;
   const int head = rest / a.ntiles;
   const int m0 = mt * B2M, n0 = nt * B2N;
+  if (m0 >= a.M || n0 >= a.N) return;  // no tile past the matrices (whole workgroup, no barrier yet)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
