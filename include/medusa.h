@@ -306,7 +306,10 @@ int medusa_tree_attention_layers(const void* q, const void* k_cache, const void*
  *   out_nodes   [B][K+1] int32 (output) root (0) then the accepted nodes, -1 after
  * Workspace: greedy keeps each node's argmax and one arrival counter per
  * sequence (zero-filled before first use); rejection sampling keeps one fp64
- * distribution per sequence.
+ * distribution per sequence and, for V <= 32768, also the root's p and each
+ * depth's q (fp64, max_depth + 1 rows per sequence) computed in parallel
+ * before the walk, which then holds p in registers.  Rejection-sampling
+ * workspaces need no initialisation.
  * ------------------------------------------------------------------------ */
 size_t medusa_accept_workspace_size(int B, int V, const medusa_tree_t* tree,
                                     float temperature);

@@ -46,6 +46,7 @@ struct AcceptArgs {
   int32_t* out_tokens;
   int32_t* out_nodes;
   double* pbuf;        // [B][V]       (rejection)
+  double* qbuf;        // [B][max_depth + 1][V] (rejection, V <= RT * 32): row 0 the root's p, row d q_d
   int32_t* argmax;     // [B][T]       (greedy)
   int* counters;       // [B], zero between calls (greedy)
 };
@@ -228,6 +229,58 @@ __device__ void softmax_into(const float* z, double tau, int V, double* p, doubl
   __syncthreads();
 }
 
+// Draw the final token from p by inverse CDF with u_sample[b][u] (chunked
+// prefix sums in thread order) and finish the sequence's outputs.
+__device__ void sample_tail(const AcceptArgs& a, int b, int u, int len, const double* p, int* shi,
+                            int32_t* otoks, int32_t* onodes) {
+  const int V = a.V;
+  const int tid = threadIdx.x;
+  const int C = (V + RT - 1) / RT;
+  const int v0 = tid * C;
+  const int v1 = min(V, v0 + C);
+  double local = 0.0;
+  for (int v = v0; v < v1; ++v) local += p[v];
+  // exclusive scan of the per-thread sums (wave scan, then wave totals)
+  const int lane = tid & 63, wave = tid >> 6;
+  double incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  __shared__ double s_wsum[RW];
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  double wave_off = 0.0, total = 0.0;
+  for (int w = 0; w < RW; ++w) {
+    if (w < wave) wave_off += s_wsum[w];
+    total += s_wsum[w];
+  }
+  const double thr = static_cast<double>(a.us[static_cast<int64_t>(b) * a.T + u]) * total;
+  double run = wave_off + incl - local;
+  int hit = 0x7fffffff, lastpos = -1;
+  for (int v = v0; v < v1; ++v) {
+    run += p[v];
+    if (run > thr) {
+      hit = v;
+      break;
+    }
+  }
+  for (int v = v0; v < v1; ++v)
+    if (p[v] > 0.0) lastpos = v;
+  hit = block_min_int(hit, shi);
+  lastpos = block_max_int(lastpos, shi);
+  if (tid == 0) {
+    const int y = (hit != 0x7fffffff) ? hit : lastpos;
+    otoks[len] = y;
+    a.acc_len[b] = len;
+    for (int j = len + 1; j < a.Kp1; ++j) {
+      otoks[j] = -1;
+      onodes[j] = -1;
+    }
+  }
+}
+
 __global__ __launch_bounds__(RT) void accept_reject_kernel(AcceptArgs a) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -299,51 +352,194 @@ __global__ __launch_bounds__(RT) void accept_reject_kernel(AcceptArgs a) {
     softmax_into(a.base + (static_cast<int64_t>(b) * a.T + u) * V, tau, V, p, shd);
   }
 
-  // inverse CDF with u_sample[b][u]: chunked prefix sums in thread order
-  const int C = (V + RT - 1) / RT;
-  const int v0 = tid * C;
-  const int v1 = min(V, v0 + C);
-  double local = 0.0;
-  for (int v = v0; v < v1; ++v) local += p[v];
-  // exclusive scan of the per-thread sums (wave scan, then wave totals)
-  const int lane = tid & 63, wave = tid >> 6;
-  double incl = local;
+  sample_tail(a, b, u, len, p, shi, otoks, onodes);
+}
+
+// ---- rejection sampling with the distributions in registers (V <= RT * PER) ----
+// The same arithmetic as accept_reject_kernel, in the same order per thread
+// (thread t owns v = t + RT * i), so every value and decision is identical.
+// First, in parallel over (row, sequence): the root's p = softmax(base / tau)
+// and each depth's q_d = softmax(head[d-1] / tau), fp64, into qbuf.  Then one
+// workgroup per sequence walks the tree with p in registers: p(x) comes from
+// its owner thread, q from qbuf, and a rejection's residual and
+// renormalisation never leave the registers.  Only the final p goes to pbuf,
+// for the inverse-CDF scan.  Rows are read and written through buffer
+// descriptors that end at the row's end (element i of a thread at the scalar
+// offset RT * i): past V a load reads 0 and a store is dropped, so padded
+// elements add exact zeros to the sums and need no guard there.
+constexpr int RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit data format
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, RSRC_WORD3);
+}
+__device__ __forceinline__ double ld_f64(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ float ld_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void st_f64(double x, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, voff, soff, 0);
+}
+
+// p = softmax(z / tau) of one row into registers (the arithmetic of
+// softmax_into, per thread in the same order); z is read twice in batches
+template <int PER>
+__device__ __forceinline__ void softmax_regs(const float* z, double tau, int V, int nv, double (&pr)[PER],
+                                             double* shd) {
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rz = row_rsrc(z, V * 4);
+  constexpr int ZB = PER < 16 ? PER : 16;
+  double mx = -INFINITY;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
+  for (int h = 0; h < PER; h += ZB) {
+    float zv[ZB];
+#pragma unroll
+    for (int j = 0; j < ZB; ++j) zv[j] = ld_f32(rz, tid * 4, RT * 4 * (h + j));
+#pragma unroll
+    for (int j = 0; j < ZB; ++j)
+      if (h + j < nv) mx = fmax(mx, static_cast<double>(zv[j]) / tau);
   }
-  __shared__ double s_wsum[RW];
-  if (lane == 63) s_wsum[wave] = incl;
+  mx = block_max(mx, shd);
+  double s = 0.0;
+#pragma unroll
+  for (int h = 0; h < PER; h += ZB) {
+    float zv[ZB];
+#pragma unroll
+    for (int j = 0; j < ZB; ++j) zv[j] = ld_f32(rz, tid * 4, RT * 4 * (h + j));
+#pragma unroll
+    for (int j = 0; j < ZB; ++j) {
+      pr[h + j] = 0.0;
+      if (h + j < nv) {
+        pr[h + j] = exp(static_cast<double>(zv[j]) / tau - mx);
+        s += pr[h + j];
+      }
+    }
+  }
+  const double Z = block_sum(s, shd);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) pr[i] = pr[i] / Z;
+}
+
+template <int PER>
+__global__ __launch_bounds__(RT) void accept_rows_kernel(AcceptArgs a) {
+  const int d = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  __shared__ double shd[RW];
+  const int V = a.V;
+  const int nv = tid < V ? (V - tid + RT - 1) / RT : 0;  // this thread's elements below V
+  const float* z = d == 0 ? a.base + static_cast<int64_t>(b) * a.T * V
+                          : a.head + (static_cast<int64_t>(b) * a.K + d - 1) * V;
+  double pr[PER];
+  softmax_regs<PER>(z, static_cast<double>(a.tau), V, nv, pr, shd);
+  const __amdgpu_buffer_rsrc_t ro =
+      row_rsrc(a.qbuf + (static_cast<int64_t>(b) * (a.max_depth + 1) + d) * V, V * 8);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) st_f64(pr[i], ro, tid * 8, RT * 8 * i);
+}
+
+template <int PER>
+__global__ __launch_bounds__(RT) void accept_walk_kernel(AcceptArgs a) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ double shd[RW];
+  __shared__ int shi[RW];
+  __shared__ double s_px;
+  const double tau = static_cast<double>(a.tau);
+  const int V = a.V;
+  const int nv = tid < V ? (V - tid + RT - 1) / RT : 0;
+  const double* qb = a.qbuf + static_cast<int64_t>(b) * (a.max_depth + 1) * V;
+  const int32_t* tk = a.toks + static_cast<int64_t>(b) * a.T;
+  double pr[PER];  // p[tid + RT * i]; 0 past V
+  {
+    const __amdgpu_buffer_rsrc_t r0 = row_rsrc(qb, V * 8);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) pr[i] = ld_f64(r0, tid * 8, RT * 8 * i);
+  }
+  int u = 0, len = 0;
+  int32_t* onodes = a.out_nodes + static_cast<int64_t>(b) * a.Kp1;
+  int32_t* otoks = a.out_tokens + static_cast<int64_t>(b) * a.Kp1;
+  if (tid == 0) onodes[0] = 0;
+  while (true) {
+    int accepted = -1;
+    // the walk is the same in every thread: node, depth and token are uniform
+    const int c_end = __builtin_amdgcn_readfirstlane(a.child_start[u + 1]);
+    for (int ci = __builtin_amdgcn_readfirstlane(a.child_start[u]); ci < c_end; ++ci) {
+      const int c = __builtin_amdgcn_readfirstlane(a.child_list[ci]);
+      const int d = __builtin_amdgcn_readfirstlane(a.depth[c]);
+      const int x = __builtin_amdgcn_readfirstlane(tk[c]);
+      const double* q = qb + static_cast<int64_t>(d) * V;
+      const double qx = q[x];
+      if (tid == x % RT) {
+        double px = 0.0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (i == x / RT) px = pr[i];
+        s_px = px;
+      }
+      __syncthreads();
+      const double px = s_px;
+      __syncthreads();  // every thread has read s_px before it is written again
+      const double alpha = (qx == 0.0) ? 1.0 : fmin(1.0, px / qx);
+      const bool take = static_cast<double>(a.ua[static_cast<int64_t>(b) * a.T + c]) < alpha;
+      if (__builtin_amdgcn_readfirstlane(static_cast<int>(take))) {  // the same in every thread
+        accepted = c;
+        break;
+      }
+      // residual max(0, p - q_d), renormalised; q in batches of 16
+      const __amdgpu_buffer_rsrc_t rq = row_rsrc(q, V * 8);
+      constexpr int QB = PER < 16 ? PER : 16;
+      double s = 0.0;
+#pragma unroll
+      for (int h = 0; h < PER; h += QB) {
+        double qv[QB];
+#pragma unroll
+        for (int j = 0; j < QB; ++j) qv[j] = ld_f64(rq, tid * 8, RT * 8 * (h + j));
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          const double r = fmax(0.0, pr[h + j] - qv[j]);  // 0 past V
+          pr[h + j] = r;
+          s += r;
+        }
+      }
+      const double Z = block_sum(s, shd);
+      if (Z > 0.0) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) pr[i] = pr[i] / Z;
+      }
+    }
+    if (accepted < 0) break;
+    if (tid == 0) {
+      otoks[len] = tk[accepted];
+      onodes[len + 1] = accepted;
+    }
+    ++len;
+    u = __builtin_amdgcn_readfirstlane(accepted);
+    softmax_regs<PER>(a.base + (static_cast<int64_t>(b) * a.T + u) * V, tau, V, nv, pr, shd);
+  }
+  // the final p to pbuf, then the same inverse-CDF scan as accept_reject_kernel
+  double* p = a.pbuf + static_cast<int64_t>(b) * V;
+  {
+    const __amdgpu_buffer_rsrc_t rp = row_rsrc(p, V * 8);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) st_f64(pr[i], rp, tid * 8, RT * 8 * i);
+  }
   __syncthreads();
-  double wave_off = 0.0, total = 0.0;
-  for (int w = 0; w < RW; ++w) {
-    if (w < wave) wave_off += s_wsum[w];
-    total += s_wsum[w];
-  }
-  const double thr = static_cast<double>(a.us[static_cast<int64_t>(b) * a.T + u]) * total;
-  double run = wave_off + incl - local;
-  int hit = 0x7fffffff, lastpos = -1;
-  for (int v = v0; v < v1; ++v) {
-    run += p[v];
-    if (run > thr) {
-      hit = v;
-      break;
-    }
-  }
-  for (int v = v0; v < v1; ++v)
-    if (p[v] > 0.0) lastpos = v;
-  hit = block_min_int(hit, shi);
-  lastpos = block_max_int(lastpos, shi);
-  if (tid == 0) {
-    const int y = (hit != 0x7fffffff) ? hit : lastpos;
-    otoks[len] = y;
-    a.acc_len[b] = len;
-    for (int j = len + 1; j < a.Kp1; ++j) {
-      otoks[j] = -1;
-      onodes[j] = -1;
-    }
-  }
+  sample_tail(a, b, u, len, p, shi, otoks, onodes);
+}
+
+// elements per thread of the register-resident rejection path (0: V too
+// large, the vocabulary stays in the workspace)
+int reject_per(int V) { return V <= RT * 8 ? 8 : V <= RT * 16 ? 16 : V <= RT * 32 ? 32 : 0; }
+
+template <int PER>
+int launch_reject_regs(const AcceptArgs& a, int B, hipStream_t stream) {
+  hipLaunchKernelGGL((accept_rows_kernel<PER>), dim3(a.max_depth + 1, B), dim3(RT), 0, stream, a);
+  int rc = check_launch("rejection-sampling rows (root p, q per depth)");
+  if (rc) return rc;
+  hipLaunchKernelGGL((accept_walk_kernel<PER>), dim3(B), dim3(RT), 0, stream, a);
+  return check_launch("rejection-sampling acceptance");
 }
 
 }  // namespace
@@ -353,7 +549,9 @@ extern "C" size_t medusa_accept_workspace_size(int B, int V, const medusa_tree_t
   if (B < 1 || V < 1 || !tree) return 0;
   if (temperature == 0.f)
     return round_up(static_cast<size_t>(B) * tree->T * 4, 256) + round_up(static_cast<size_t>(B) * 4, 256);
-  return round_up(static_cast<size_t>(B) * V * sizeof(double), 256);
+  size_t n = round_up(static_cast<size_t>(B) * V * sizeof(double), 256);
+  if (reject_per(V)) n += round_up(static_cast<size_t>(B) * (tree->max_depth + 1) * V * sizeof(double), 256);
+  return n;
 }
 
 extern "C" int medusa_accept_paths(const float* base_logits, const float* head_logits,
@@ -405,6 +603,17 @@ extern "C" int medusa_accept_paths(const float* base_logits, const float* head_l
     return check_launch("greedy acceptance");
   }
   a.pbuf = static_cast<double*>(ws);
-  hipLaunchKernelGGL(accept_reject_kernel, dim3(B), dim3(RT), 0, stream, a);
-  return check_launch("rejection-sampling acceptance");
+  switch (reject_per(V)) {
+    case 8:
+    case 16:
+    case 32:
+      a.qbuf = reinterpret_cast<double*>(static_cast<char*>(ws) +
+                                         round_up(static_cast<size_t>(B) * V * sizeof(double), 256));
+      if (reject_per(V) == 8) return launch_reject_regs<8>(a, B, stream);
+      if (reject_per(V) == 16) return launch_reject_regs<16>(a, B, stream);
+      return launch_reject_regs<32>(a, B, stream);
+    default:
+      hipLaunchKernelGGL(accept_reject_kernel, dim3(B), dim3(RT), 0, stream, a);
+      return check_launch("rejection-sampling acceptance");
+  }
 }

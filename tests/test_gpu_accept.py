@@ -117,3 +117,15 @@ def test_accept_argument_errors():
     with pytest.raises(api.MedusaError) as e:
         api.accept_paths(base, None, toks, t, None, None, -1.0)
     assert e.value.code == api.EINVAL
+
+
+@pytest.mark.parametrize("V", [9000, 32768, 40000])
+@pytest.mark.parametrize("tau", [0.7, 1.0])
+def test_accept_rejection_vocab_sizes(V, tau):
+    """Rejection sampling keeps the distribution in registers up to 32768
+    entries (8, 16 or 32 per thread) and in the workspace above; each size
+    class against the oracle, with planted acceptances so that walks go deep."""
+    w = synth.WORKLOADS["tiny-fp32"].scaled(B=3, V=V, K=3, topk=(4, 3, 2), T=14, cfg_id=470 + V % 97)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    for seed in range(3):
+        _compare(w, parent, rank, tau, seed)
