@@ -356,14 +356,16 @@ __global__ __launch_bounds__(RT) void accept_reject_kernel(AcceptArgs a) {
 }
 
 // ---- rejection sampling with the distributions in registers (V <= RT * PER) ----
-// The same arithmetic as accept_reject_kernel, in the same order per thread
-// (thread t owns v = t + RT * i), so every value and decision is identical.
+// The formulas of accept_reject_kernel, per thread in the same order (thread
+// t owns v = t + RT * i), except that each division by tau or by a row sum
+// is a multiplication by its reciprocal (one rounding apart: fp64 values
+// agree to an ulp, decisions agree except at ties of that size).
 // First, in parallel over (row, sequence): the root's p = softmax(base / tau)
 // and each depth's q_d = softmax(head[d-1] / tau), fp64, into qbuf.  Then one
 // workgroup per sequence walks the tree with p in registers: p(x) comes from
 // its owner thread, q from qbuf, and a rejection's residual and
-// renormalisation never leave the registers.  Only the final p goes to pbuf,
-// for the inverse-CDF scan.  Rows are read and written through buffer
+// renormalisation never leave the registers, nor does the final
+// inverse-CDF draw.  Rows are read and written through buffer
 // descriptors that end at the row's end (element i of a thread at the scalar
 // offset RT * i): past V a load reads 0 and a store is dropped, so padded
 // elements add exact zeros to the sums and need no guard there.
@@ -386,7 +388,7 @@ __device__ __forceinline__ void st_f64(double x, __amdgpu_buffer_rsrc_t r, int v
 // p = softmax(z / tau) of one row into registers (the arithmetic of
 // softmax_into, per thread in the same order); z is read twice in batches
 template <int PER>
-__device__ __forceinline__ void softmax_regs(const float* z, double tau, int V, int nv, double (&pr)[PER],
+__device__ __forceinline__ void softmax_regs(const float* z, double inv_tau, int V, int nv, double (&pr)[PER],
                                              double* shd) {
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t rz = row_rsrc(z, V * 4);
@@ -399,7 +401,7 @@ __device__ __forceinline__ void softmax_regs(const float* z, double tau, int V, 
     for (int j = 0; j < ZB; ++j) zv[j] = ld_f32(rz, tid * 4, RT * 4 * (h + j));
 #pragma unroll
     for (int j = 0; j < ZB; ++j)
-      if (h + j < nv) mx = fmax(mx, static_cast<double>(zv[j]) / tau);
+      if (h + j < nv) mx = fmax(mx, static_cast<double>(zv[j]) * inv_tau);
   }
   mx = block_max(mx, shd);
   double s = 0.0;
@@ -412,14 +414,14 @@ __device__ __forceinline__ void softmax_regs(const float* z, double tau, int V, 
     for (int j = 0; j < ZB; ++j) {
       pr[h + j] = 0.0;
       if (h + j < nv) {
-        pr[h + j] = exp(static_cast<double>(zv[j]) / tau - mx);
+        pr[h + j] = exp(static_cast<double>(zv[j]) * inv_tau - mx);
         s += pr[h + j];
       }
     }
   }
-  const double Z = block_sum(s, shd);
+  const double inv_z = 1.0 / block_sum(s, shd);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) pr[i] = pr[i] / Z;
+  for (int i = 0; i < PER; ++i) pr[i] *= inv_z;
 }
 
 template <int PER>
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(RT) void accept_rows_kernel(AcceptArgs a) {
   const float* z = d == 0 ? a.base + static_cast<int64_t>(b) * a.T * V
                           : a.head + (static_cast<int64_t>(b) * a.K + d - 1) * V;
   double pr[PER];
-  softmax_regs<PER>(z, static_cast<double>(a.tau), V, nv, pr, shd);
+  softmax_regs<PER>(z, 1.0 / static_cast<double>(a.tau), V, nv, pr, shd);
   const __amdgpu_buffer_rsrc_t ro =
       row_rsrc(a.qbuf + (static_cast<int64_t>(b) * (a.max_depth + 1) + d) * V, V * 8);
 #pragma unroll
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(RT) void accept_walk_kernel(AcceptArgs a) {
   __shared__ double shd[RW];
   __shared__ int shi[RW];
   __shared__ double s_px;
-  const double tau = static_cast<double>(a.tau);
+  const double inv_tau = 1.0 / static_cast<double>(a.tau);
   const int V = a.V;
   const int nv = tid < V ? (V - tid + RT - 1) / RT : 0;
   const double* qb = a.qbuf + static_cast<int64_t>(b) * (a.max_depth + 1) * V;
@@ -505,8 +507,9 @@ __global__ __launch_bounds__(RT) void accept_walk_kernel(AcceptArgs a) {
       }
       const double Z = block_sum(s, shd);
       if (Z > 0.0) {
+        const double inv_z = 1.0 / Z;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) pr[i] = pr[i] / Z;
+        for (int i = 0; i < PER; ++i) pr[i] *= inv_z;
       }
     }
     if (accepted < 0) break;
@@ -516,17 +519,70 @@ __global__ __launch_bounds__(RT) void accept_walk_kernel(AcceptArgs a) {
     }
     ++len;
     u = __builtin_amdgcn_readfirstlane(accepted);
-    softmax_regs<PER>(a.base + (static_cast<int64_t>(b) * a.T + u) * V, tau, V, nv, pr, shd);
+    softmax_regs<PER>(a.base + (static_cast<int64_t>(b) * a.T + u) * V, inv_tau, V, nv, pr, shd);
   }
-  // the final p to pbuf, then the same inverse-CDF scan as accept_reject_kernel
-  double* p = a.pbuf + static_cast<int64_t>(b) * V;
-  {
-    const __amdgpu_buffer_rsrc_t rp = row_rsrc(p, V * 8);
+  // Inverse CDF from the registers: the smallest v with cumsum(p)[v] >
+  // u_sample * sum(p), else the last v with p > 0.  The vocabulary is taken
+  // in groups of 8 rows (8192 entries) staged through LDS in v order; thread
+  // t sums entries 8t .. 8t+7 of the group, an exclusive block scan gives
+  // each thread the sum before them, and the first group that crosses the
+  // threshold ends the search.
+  double tsum = 0.0;
+  int lastpos = -1;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) st_f64(pr[i], rp, tid * 8, RT * 8 * i);
+  for (int i = 0; i < PER; ++i) {
+    tsum += pr[i];
+    if (pr[i] > 0.0) lastpos = tid + RT * i;
   }
-  __syncthreads();
-  sample_tail(a, b, u, len, p, shi, otoks, onodes);
+  const double total = block_sum(tsum, shd);
+  lastpos = block_max_int(lastpos, shi);
+  const double thr = static_cast<double>(a.us[static_cast<int64_t>(b) * a.T + u]) * total;
+  __shared__ double s_grp[8 * RT];
+  __shared__ double s_wsum[RW];
+  const int lane = tid & 63, wave = tid >> 6;
+  double before_grp = 0.0;  // cumsum before the group (the same in every thread)
+  int hit = 0x7fffffff;
+#pragma unroll
+  for (int g = 0; g < PER; g += 8) {
+    __syncthreads();  // the previous group's reads are done
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_grp[j * RT + tid] = pr[g + j];  // entry v - RT*g
+    __syncthreads();
+    double loc = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) loc += s_grp[8 * tid + k];
+    double incl = loc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    double wave_off = 0.0, gtot = 0.0;
+    for (int w = 0; w < RW; ++w) {
+      if (w < wave) wave_off += s_wsum[w];
+      gtot += s_wsum[w];
+    }
+    double run = before_grp + wave_off + incl - loc;
+    int h = 0x7fffffff;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      run += s_grp[8 * tid + k];
+      if (run > thr && h == 0x7fffffff) h = RT * g + 8 * tid + k;
+    }
+    hit = block_min_int(h, shi);
+    if (hit != 0x7fffffff) break;
+    before_grp += gtot;
+  }
+  if (tid == 0) {
+    otoks[len] = (hit != 0x7fffffff) ? hit : lastpos;
+    a.acc_len[b] = len;
+    for (int j = len + 1; j < a.Kp1; ++j) {
+      otoks[j] = -1;
+      onodes[j] = -1;
+    }
+  }
 }
 
 // elements per thread of the register-resident rejection path (0: V too
