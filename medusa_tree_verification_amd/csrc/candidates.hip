@@ -48,49 +48,6 @@ struct CandArgs {
   int rows;              // B * K
 };
 
-// Wave-wide arg-max of (value, index) pairs (larger value, then lower index),
-// left in every lane.  All on the vector ALU: DPP quad permutes pair lanes
-// that differ in bit 0 and bit 1, the half-row and row mirrors then pair
-// uniform groups of 4 and 8, and the 16- and 32-lane swaps finish across rows.
-__device__ __forceinline__ void best_of(float& bv, int& bi, float ov, int oi) {
-  const bool take = ov > bv || (ov == bv && oi < bi);
-  bv = take ? ov : bv;
-  bi = take ? oi : bi;
-}
-
-template <int CTRL>
-__device__ __forceinline__ void best_dpp(float& bv, int& bi) {
-  const float ov = __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(bv), CTRL, 0xf, 0xf, false));
-  const int oi = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xf, 0xf, false);
-  best_of(bv, bi, ov, oi);
-}
-
-__device__ __forceinline__ void wave_best(float& bv, int& bi) {
-  best_dpp<0xB1>(bv, bi);   // quad_perm [1,0,3,2]
-  best_dpp<0x4E>(bv, bi);   // quad_perm [2,3,0,1]
-  best_dpp<0x141>(bv, bi);  // row_half_mirror
-  best_dpp<0x140>(bv, bi);  // row_mirror
-  {
-    // rows 0<->1 and 2<->3: both halves of the swap carry one candidate each
-    const auto v = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
-    const auto i = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(bi), static_cast<unsigned>(bi), false, false);
-    float av = __uint_as_float(v[0]);
-    int ai = static_cast<int>(i[0]);
-    best_of(av, ai, __uint_as_float(v[1]), static_cast<int>(i[1]));
-    bv = av;
-    bi = ai;
-  }
-  {
-    const auto v = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
-    const auto i = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(bi), static_cast<unsigned>(bi), false, false);
-    float av = __uint_as_float(v[0]);
-    int ai = static_cast<int>(i[0]);
-    best_of(av, ai, __uint_as_float(v[1]), static_cast<int>(i[1]));
-    bv = av;
-    bi = ai;
-  }
-}
-
 // the lane holding the popped winner drops it from its list
 template <int KM>
 __device__ __forceinline__ void list_pop_if(float (&tv)[KM], int (&ti)[KM], float bv, int bi) {

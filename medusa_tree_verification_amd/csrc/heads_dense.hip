@@ -572,12 +572,29 @@ __global__ __launch_bounds__(256) void dense_topk_merge(MergeArgs a) {
   if constexpr (LISTS) {
     const float* v = a.v + static_cast<int64_t>(row) * a.nlist * a.kmax;
     const int32_t* ix = a.ix + static_cast<int64_t>(row) * a.nlist * a.kmax;
-    for (int l = lane; l < a.nlist; l += 64) {
-      for (int s = 0; s < a.kmax; ++s) {
-        const float x = v[l * a.kmax + s];
-        if (!(x > tv[KM - 1])) break;
-        list_insert<KM>(tv, ti, x, ix[l * a.kmax + s]);
+    // each list whole in registers, the next one's loads issued before this
+    // one is inserted; a sorted list: once an entry stays out, so do the rest
+    float xv[2][KM];
+    int xi[2][KM];
+    auto load = [&](int l, float (&dv)[KM], int (&di)[KM]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int s = 0; s < KM; ++s) {
+        const bool in = l < a.nlist && s < a.kmax;
+        dv[s] = in ? v[l * a.kmax + s] : -INFINITY;
+        di[s] = in ? ix[l * a.kmax + s] : 0x7fffffff;
       }
+    };
+    auto absorb = [&](const float (&dv)[KM], const int (&di)[KM]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int s = 0; s < KM; ++s)
+        if (dv[s] > tv[KM - 1]) list_insert<KM>(tv, ti, dv[s], di[s]);
+    };
+    load(lane, xv[0], xi[0]);
+    for (int l = lane; l < a.nlist; l += 128) {
+      load(l + 64, xv[1], xi[1]);
+      absorb(xv[0], xi[0]);
+      load(l + 128, xv[0], xi[0]);
+      absorb(xv[1], xi[1]);
     }
   } else {
     const float* v = a.v + static_cast<int64_t>(row) * a.N;
@@ -592,14 +609,7 @@ __global__ __launch_bounds__(256) void dense_topk_merge(MergeArgs a) {
   for (int s = 0; s < a.kmax_out; ++s) {
     float bv = tv[0];
     int bi = ti[0];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ovv = __shfl_xor(bv, off);
-      const int oii = __shfl_xor(bi, off);
-      const bool take = ovv > bv || (ovv == bv && oii < bi);
-      bv = take ? ovv : bv;
-      bi = take ? oii : bi;
-    }
+    wave_best(bv, bi);
     if (s < kd) {
       if (lane == 0) {
         oi[s] = bi;
