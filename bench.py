@@ -347,8 +347,8 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path's multi-GPU "
-              "sharding is described in DESIGN.md but not built", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library runs the "
+              "verify step on one GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     from medusa_tree_verification_amd import synth
     w = synth.WORKLOADS[args.workload]

@@ -15,7 +15,7 @@ r < alpha); on rejection a token is drawn from the residual
 p'(x) = max(0, p(x) - q(x)) / sum_y max(0, p(y) - q(y)).  P3 section 2 proves
 that the result is distributed as p.
 
-On a tree (readings, listed in the design doc):
+On a tree (readings where the pages leave the step open):
   * node 0 is the root (already decided); its base logits give p for depth 1;
   * the children of the current node are tried one by one in rank order; a
     rejection replaces p by the residual max(0, p - q_d) (normalised) before

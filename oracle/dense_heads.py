@@ -5,7 +5,7 @@ Medusa 헤드 구조": head k turns a hidden state into logits through its resid
 SiLU block and its vocab projection; section "소스코드 레벨 구조 분석"
 (``generate_candidates``) keeps the top-k of every head's logits.
 
-Reading (listed in the design doc): the dense variant runs the same K heads on the
+Reading (the pages leave it open): the dense variant runs the same K heads on the
 hidden state of every tree token -- M = B*T rows instead of B -- so that the
 next step's candidates already exist at whichever node gets accepted.  Head d
 keeps k_d candidates (the tree's per-depth top-k), by descending logit with

@@ -9,7 +9,7 @@ equations leave open: both projections are bias-free linear layers stored
 ``generate_candidates`` takes top-k of the *logits* (softmax is monotone, so it
 is deferred to acceptance).
 
-Readings (listed in DESIGN.md):
+Readings (where the pages are silent):
   * weights are [out, in]; ``h W`` in the equation is W @ h with W [out, in];
   * SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a));
   * in bf16 workloads the residual output r is rounded to bf16 (round to
