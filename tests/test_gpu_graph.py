@@ -151,3 +151,52 @@ def test_graph_replays_of_the_other_calls():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(outs, ref)):
             assert torch.equal(a, b), f"replay {rep}: output {i} differs from eager"
+
+
+@pytest.mark.parametrize("V", [5000, 40000])
+def test_graph_replays_rejection_sampling(V):
+    """Rejection-sampling acceptance (its two kernels, registers path, and
+    the one-kernel path above 32768 entries) captured and replayed four
+    times with eager work between, each replay equal to the eager result."""
+    w = synth.WORKLOADS["tiny-fp32"].scaled(B=3, V=V, K=3, topk=(4, 3, 2), T=14, cfg_id=480)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    tree = api.Tree(parent, rank, w.topk)
+    toks_np = synth.tree_tokens_input(w, parent, 1)
+    base, head, ua, us = synth.accept_inputs(w, parent, toks_np, "cpu", plant=True, seed_extra=1)
+    base, head, ua, us = base.to(DEV), head.to(DEV), ua.to(DEV), us.to(DEV)
+    toks = torch.from_numpy(toks_np).to(DEV)
+    acc = (torch.empty(w.B, dtype=torch.int32, device=DEV),
+           torch.empty((w.B, w.K + 1), dtype=torch.int32, device=DEV),
+           torch.empty((w.B, w.K + 1), dtype=torch.int32, device=DEV))
+    ws = torch.zeros(api.accept_workspace_size(w.B, w.V, tree, 0.7), dtype=torch.uint8, device=DEV)
+
+    def run():
+        api.accept_paths(base, head, toks, tree, ua, us, 0.7, outs=acc, ws=ws)
+
+    announce("graph: rejection eager", V)
+    run()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in acc]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for x in acc:
+            x.fill_(-7)
+        ws.zero_()
+        torch.cuda.synchronize()
+        announce("graph: rejection replay", V, rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(acc, ref):
+            assert torch.equal(a, b), f"replay {rep} differs from eager"
+        run()
+        torch.cuda.synchronize()
+        for a, b in zip(acc, ref):
+            assert torch.equal(a, b), f"eager call after replay {rep} differs"
