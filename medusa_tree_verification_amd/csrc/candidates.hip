@@ -12,14 +12,13 @@
 // result is unique and bit-exact.
 //
 // Two kernels spread every logit row over many CUs:
-//   1. one wave per (sequence, head, chunk of CW columns): each lane keeps a
-//      sorted list of its largest values, taking its columns in increasing
-//      order (a value enters only if strictly larger, so an equal logit of a
-//      later column stays behind); the chunk's top-kmax is then popped from
-//      the 64 lane lists by kmax wave-wide arg-max rounds and written as a
-//      sorted (logit, column) list;
+//   1. one wave per (sequence, head, chunk of CW columns): each lane sorts its
+//      8 (logit, column) pairs under that order; the chunk's top-kmax is then
+//      popped from the 64 lane lists by kmax wave-wide arg-max rounds and
+//      written as a sorted (logit, column) list;
 //   2. one wave per (sequence, head): the chunk lists (in column order) go
-//      into per-lane lists the same way, k_d arg-max rounds pop the head's
+//      into per-lane lists the same way (with at most 64 chunks each lane's
+//      chunk list already is its sorted list), k_d arg-max rounds pop the head's
 //      candidates, and the same wave writes them, the tree tokens of the
 //      nodes at depth head+1, and (head 0) the root and every position.
 // The chunk lists live in the caller's workspace.
@@ -85,13 +84,38 @@ __global__ __launch_bounds__(256) void cand_chunks(CandArgs a) {
     const int c = c0 + 64 * i + lane;
     v[i] = c < a.V ? x[c] : -INFINITY;
   }
+  // the lane's 8 (logit, column) pairs sorted by a 19-comparator odd-even
+  // merge network under the total order (columns past V sort last as
+  // padding); the lane list keeps the first min(KM, 8) -- a lane cannot hold
+  // more than kmax <= KM of the chunk's top-kmax
+  static_assert(CW / 64 == 8, "the sorting network takes 8 values per lane");
+  float sv[8];
+  int si[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = c0 + 64 * i + lane;
+    sv[i] = c < a.V ? v[i] : -INFINITY;
+    si[i] = c < a.V ? c : 0x7fffffff;
+  }
+  auto cmpx = [&](int i, int j) __attribute__((always_inline)) {  // (i, j) in order afterwards
+    const bool sw = sv[j] > sv[i] || (sv[j] == sv[i] && si[j] < si[i]);
+    const float fv = sw ? sv[j] : sv[i], bv = sw ? sv[i] : sv[j];
+    const int fi = sw ? si[j] : si[i], bi = sw ? si[i] : si[j];
+    sv[i] = fv; sv[j] = bv; si[i] = fi; si[j] = bi;
+  };
+  cmpx(0, 1); cmpx(2, 3); cmpx(4, 5); cmpx(6, 7);
+  cmpx(0, 2); cmpx(1, 3); cmpx(4, 6); cmpx(5, 7);
+  cmpx(1, 2); cmpx(5, 6);
+  cmpx(0, 4); cmpx(1, 5); cmpx(2, 6); cmpx(3, 7);
+  cmpx(2, 4); cmpx(3, 5);
+  cmpx(1, 2); cmpx(3, 4); cmpx(5, 6);
   float tv[KM];
   int ti[KM];
   list_init<KM>(tv, ti);
 #pragma unroll
-  for (int i = 0; i < CW / 64; ++i) {
-    const int c = c0 + 64 * i + lane;
-    if (v[i] > tv[KM - 1] && c < a.V) list_insert<KM>(tv, ti, v[i], c);
+  for (int i = 0; i < (KM < 8 ? KM : 8); ++i) {
+    tv[i] = sv[i];
+    ti[i] = si[i];
   }
   const int64_t base = (static_cast<int64_t>(row) * a.nchunks + chunk) * a.kmax;
   for (int s = 0; s < a.kmax; ++s) {
@@ -112,27 +136,43 @@ __global__ __launch_bounds__(256) void cand_merge_tree(CandArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // = b * K + d
   if (row >= a.rows) return;                              // whole wave, no barrier
   const int b = row / a.K, d = row % a.K;
-  // the first 64 nodes' depth and rank are loaded now and used after the pops
+  // the first 64 nodes' depth and rank, the context length and the root are
+  // loaded now and used after the pops
   const int dn0 = lane < a.T ? a.depth[lane] : -1;
   const int rn0 = lane < a.T ? a.rank[lane] : 0;
+  const int ctx_b = a.ctx[b];
+  const int root_b = a.root[b];
   const int kd = a.kpd[d];
   float tv[KM];
   int ti[KM];
   list_init<KM>(tv, ti);
   const float* cv = a.cv + static_cast<int64_t>(row) * a.nchunks * a.kmax;
   const int32_t* ci = a.ci + static_cast<int64_t>(row) * a.nchunks * a.kmax;
-  for (int l = lane; l < a.nchunks; l += 64) {
-    float xv[KM];
-    int xi[KM];
+  if (a.nchunks <= 64) {
+    // one chunk list per lane, already sorted: it is the lane's list
+    if (lane < a.nchunks) {
 #pragma unroll
-    for (int s = 0; s < KM; ++s) {  // the whole chunk list in flight at once
-      xv[s] = s < a.kmax ? cv[l * a.kmax + s] : -INFINITY;
-      xi[s] = s < a.kmax ? ci[l * a.kmax + s] : 0x7fffffff;
+      for (int s = 0; s < KM; ++s) {
+        if (s < a.kmax) {
+          tv[s] = cv[lane * a.kmax + s];
+          ti[s] = ci[lane * a.kmax + s];
+        }
+      }
     }
-    // a sorted list: once an entry stays out, every later one does too
+  } else {
+    for (int l = lane; l < a.nchunks; l += 64) {
+      float xv[KM];
+      int xi[KM];
 #pragma unroll
-    for (int s = 0; s < KM; ++s)
-      if (xv[s] > tv[KM - 1]) list_insert<KM>(tv, ti, xv[s], xi[s]);
+      for (int s = 0; s < KM; ++s) {  // the whole chunk list in flight at once
+        xv[s] = s < a.kmax ? cv[l * a.kmax + s] : -INFINITY;
+        xi[s] = s < a.kmax ? ci[l * a.kmax + s] : 0x7fffffff;
+      }
+      // a sorted list: once an entry stays out, every later one does too
+#pragma unroll
+      for (int s = 0; s < KM; ++s)
+        if (xv[s] > tv[KM - 1]) list_insert<KM>(tv, ti, xv[s], xi[s]);
+    }
   }
   // k_d arg-max rounds; lane s keeps the head's candidate of rank s
   int mine = -1;
@@ -154,10 +194,9 @@ __global__ __launch_bounds__(256) void cand_merge_tree(CandArgs a) {
     if (dn == d + 1) tok[n] = t;
   }
   if (d == 0) {
-    const int c = a.ctx[b];
     for (int n = lane; n < a.T; n += 64) {
-      a.pos[static_cast<int64_t>(b) * a.T + n] = c + a.depth[n];
-      if (n == 0) tok[0] = a.root[b];
+      a.pos[static_cast<int64_t>(b) * a.T + n] = ctx_b + (n < 64 ? dn0 : a.depth[n]);
+      if (n == 0) tok[0] = root_b;
     }
   }
 }
