@@ -74,14 +74,16 @@ struct DenseArgs {
   float* logits;        // optional [M][K][N]
 };
 
-template <int BM, int EPI, int KM>
+template <int BM, int EPI, int KM, int BNT = BN>
 __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
+  static_assert(BNT == BN || EPI == EPI_RESID, "the top-k epilogue takes 128-column tiles");
   constexpr int MT = BM / 32;         // 16-row activation tiles per wave
+  constexpr int NJ = BNT / 32;        // 16-column output tiles per wave
   constexpr int XCH = BM * 8 / 256;   // 16-byte X chunks per thread per step
-  constexpr int WCH = BN * 8 / 256;   // 16-byte W chunks per thread per step
+  constexpr int WCH = BNT * 8 / 256;  // 16-byte W chunks per thread per step
   constexpr int CH = XCH + WCH;
   constexpr int XT = BM * TROW;       // X tile bytes (W tile follows)
-  constexpr int STAGE = (BM + BN) * TROW;
+  constexpr int STAGE = (BM + BNT) * TROW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int id = blockIdx.x;
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
   const int rest = task / a.mtiles;
   const int nt = rest % a.ntiles;
   const int head = rest / a.ntiles;
-  const int m0 = mt * BM, n0 = nt * BN;
+  const int m0 = mt * BM, n0 = nt * BNT;
   if (m0 >= a.M || n0 >= a.N) return;  // no tile past the matrices (whole workgroup, no barrier yet)
 
   const int tid = threadIdx.x;
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
 
   const uint16_t* xb = a.x + head * a.x_hstride + static_cast<int64_t>(m0) * a.Kd;
   const uint16_t* wb = a.w + head * a.w_hstride + static_cast<int64_t>(n0) * a.Kd;
-  const int xrows = min(BM, a.M - m0), wrows = min(BN, a.N - n0);
+  const int xrows = min(BM, a.M - m0), wrows = min(BNT, a.N - n0);
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xb), 0, xrows * a.Kd * 2, RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t rw =
@@ -127,30 +129,30 @@ __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
     for (int u = 0; u < CH; ++u) *reinterpret_cast<uint4*>(st + loff[u]) = R[u];
   };
 
-  f32x4 acc[MT][4];
+  f32x4 acc[MT][NJ];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // operand rows: W wc*64 + 16j + l16, X wr*(BM/2) + 16i + l16; chunk 4s + g
+  // operand rows: W wc*(BNT/2) + 16j + l16, X wr*(BM/2) + 16i + l16; chunk 4s + g
   const int sw = (l16 >> 1) & 7;
   const int cx0 = 16 * (g ^ sw), cx1 = 16 * ((4 + g) ^ sw);
-  const int wrow = XT + (wc * 64 + l16) * TROW;
+  const int wrow = XT + (wc * (BNT / 2) + l16) * TROW;
   const int xrow = (wr * (BM / 2) + l16) * TROW;
   auto compute = [&](const char* st) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int cx = s ? cx1 : cx0;
-      bf16x8 wf[4], xf[MT];
+      bf16x8 wf[NJ], xf[MT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[j] = as_bf16x8(*reinterpret_cast<const uint4*>(st + wrow + j * 16 * TROW + cx));
+      for (int j = 0; j < NJ; ++j) wf[j] = as_bf16x8(*reinterpret_cast<const uint4*>(st + wrow + j * 16 * TROW + cx));
 #pragma unroll
       for (int i = 0; i < MT; ++i) xf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(st + xrow + i * 16 * TROW + cx));
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
     }
   };
 
@@ -184,8 +186,8 @@ __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
       const int m = m0 + wr * (BM / 2) + 16 * i + l16;
       if (m >= a.M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wc * 64 + 16 * j + 4 * g;
+      for (int j = 0; j < NJ; ++j) {
+        const int n = n0 + wc * (BNT / 2) + 16 * j + 4 * g;
         if (n >= a.N) continue;  // N % 4 == 0: all 4 columns are in range
         const uint2 hv = *reinterpret_cast<const uint2*>(a.hid + static_cast<int64_t>(m) * a.Kd + n);
         float o[4];
@@ -698,20 +700,20 @@ DensePlan dense_plan(int M, int H, int V, int K, int kmax, medusa_dtype_t dt) {
 
 // LDS: the two staging buffers, then (vocab projection) the fp32 tile and
 // the per-thread candidate lists, each reusing the same bytes
-template <int BM, int EPI, int KM>
+template <int BM, int EPI, int KM, int BNT = BN>
 constexpr int dense_lds() {
-  constexpr int stage = 2 * (BM + BN) * TROW;
+  constexpr int stage = 2 * (BM + BNT) * TROW;
   constexpr int tile = EPI == EPI_TOPK ? BM * BN * 4 : 0;
   constexpr int lists = EPI == EPI_TOPK ? 2 * 256 * KM * 4 : 0;
   return stage > tile ? (stage > lists ? stage : lists) : (tile > lists ? tile : lists);
 }
 
-template <int BM, int EPI, int KM>
+template <int BM, int EPI, int KM, int BNT = BN>
 int launch_gemm(const DenseArgs& a, hipStream_t s, const char* what) {
-  constexpr int lds = dense_lds<BM, EPI, KM>();
+  constexpr int lds = dense_lds<BM, EPI, KM, BNT>();
   static_assert(lds <= 64 * 1024, "dense heads LDS above the default limit");
   const int grid = 8 * a.per_xcd;
-  hipLaunchKernelGGL((dense_gemm_bf16<BM, EPI, KM>), dim3(grid), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((dense_gemm_bf16<BM, EPI, KM, BNT>), dim3(grid), dim3(256), lds, s, a);
   return check_launch(what);
 }
 
@@ -858,14 +860,17 @@ extern "C" int medusa_heads_dense(const void* hidden, const void* w1, int64_t w1
   a.w = static_cast<const uint16_t*>(w1);
   a.w_hstride = w1_head_stride;
   a.N = H;
-  a.ntiles = (H + (p.big ? B2N : BN) - 1) / (p.big ? B2N : BN);
+  // (64-column tiles on the small-tile path: at H = 4096 the 128-column ones
+  // give too few workgroups to fill the chip)
+  constexpr int RBN = 64;
+  a.ntiles = p.big ? (H + B2N - 1) / B2N : (H + RBN - 1) / RBN;
   a.tasks = p.mtiles * a.ntiles * K;
   a.per_xcd = (a.tasks + 7) / 8;
   a.hid = static_cast<const uint16_t*>(hidden);
   a.r_out = reinterpret_cast<uint16_t*>(w);
   if (p.big) rc = launch_big<EPI_RESID, 4>(a, stream, "dense heads residual block (256 x 256 tiles)");
-  else if (p.BM == 64) rc = launch_gemm<64, EPI_RESID, 4>(a, stream, "dense heads residual block");
-  else rc = launch_gemm<128, EPI_RESID, 4>(a, stream, "dense heads residual block");
+  else if (p.BM == 64) rc = launch_gemm<64, EPI_RESID, 4, RBN>(a, stream, "dense heads residual block");
+  else rc = launch_gemm<128, EPI_RESID, 4, RBN>(a, stream, "dense heads residual block");
   if (rc) return rc;
   // stage 2: logits tiles of every head and their per-tile top-kmax
   DenseArgs b = a;
