@@ -299,7 +299,8 @@ int medusa_tree_attention_layers(const void* q, const void* k_cache, const void*
  *
  *   base_logits [B][T][V] fp32   target logits after each tree node
  *   head_logits [B][K][V] fp32   (rejection only; NULL allowed for greedy)
- *   tree_tokens [B][T] int32
+ *   tree_tokens [B][T] int32 (rejection sampling clamps a token outside 0..V-1
+ *               into that range, so no access leaves the logits)
  *   u_accept, u_sample [B][T] fp32 in [0, 1) (rejection only; may be NULL for greedy)
  *   accept_len  [B] int32 (output) number of accepted tree nodes, 0..max depth
  *   out_tokens  [B][K+1] int32 (output) accept_len + 1 emitted tokens, -1 after

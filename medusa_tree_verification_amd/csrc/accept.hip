@@ -319,7 +319,7 @@ __global__ __launch_bounds__(RT) void accept_reject_kernel(AcceptArgs a) {
     for (int ci = a.child_start[u]; ci < a.child_start[u + 1]; ++ci) {
       const int c = a.child_list[ci];
       const int d = a.depth[c];
-      const int x = tk[c];
+      const int x = min(max(tk[c], 0), V - 1);  // a token outside the vocabulary is clamped
       const float* h = hb + static_cast<int64_t>(d - 1) * V;
       const double mq = s_mq[d], zq = s_zq[d];
       const double qx = exp(static_cast<double>(h[x]) / tau - mq) / zq;
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(RT) void accept_reject_kernel(AcceptArgs a) {
     }
     if (accepted < 0) break;
     if (tid == 0) {
-      otoks[len] = tk[accepted];
+      otoks[len] = min(max(tk[accepted], 0), V - 1);
       onodes[len + 1] = accepted;
     }
     ++len;
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(RT) void accept_walk_kernel(AcceptArgs a) {
     for (int ci = __builtin_amdgcn_readfirstlane(a.child_start[u]); ci < c_end; ++ci) {
       const int c = __builtin_amdgcn_readfirstlane(a.child_list[ci]);
       const int d = __builtin_amdgcn_readfirstlane(a.depth[c]);
-      const int x = __builtin_amdgcn_readfirstlane(tk[c]);
+      const int x = __builtin_amdgcn_readfirstlane(min(max(tk[c], 0), V - 1));  // clamped to the vocabulary
       const double* q = qb + static_cast<int64_t>(d) * V;
       const double qx = q[x];
       if (tid == x % RT) {
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(RT) void accept_walk_kernel(AcceptArgs a) {
     }
     if (accepted < 0) break;
     if (tid == 0) {
-      otoks[len] = tk[accepted];
+      otoks[len] = min(max(tk[accepted], 0), V - 1);
       onodes[len + 1] = accepted;
     }
     ++len;

@@ -129,3 +129,27 @@ def test_accept_rejection_vocab_sizes(V, tau):
     parent, rank = synth.cost_ordered_tree(w.topk, w.T)
     for seed in range(3):
         _compare(w, parent, rank, tau, seed)
+
+
+def test_accept_rejection_clamps_out_of_range_tokens():
+    """Rejection sampling reads p(x) and q(x) at each draft token x; a token
+    outside 0..V-1 is clamped into the vocabulary (no access leaves the
+    logits), so the call equals the call with the clamped tokens."""
+    for V in (1024, 40000):  # registers path and workspace path
+        w = synth.WORKLOADS["tiny-fp32"].scaled(B=2, V=V, K=3, topk=(4, 3, 2), T=14, cfg_id=490)
+        parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+        t = api.Tree(parent, rank, w.topk)
+        toks = synth.tree_tokens_input(w, parent, 2)
+        base, head, ua, us = synth.accept_inputs(w, parent, toks, "cpu", plant=True, seed_extra=2)
+        bad = toks.copy()
+        bad[0, 1] = -5
+        bad[1, 2] = V + 7
+        good = np.clip(bad, 0, V - 1)
+        announce("accept clamps tokens", V)
+        r_bad = api.accept_paths(base.to(DEV), head.to(DEV), torch.from_numpy(bad).to(DEV), t,
+                                 ua.to(DEV), us.to(DEV), 1.0)
+        r_good = api.accept_paths(base.to(DEV), head.to(DEV), torch.from_numpy(good).to(DEV), t,
+                                  ua.to(DEV), us.to(DEV), 1.0)
+        torch.cuda.synchronize()
+        for a, b in zip(r_bad, r_good):
+            assert torch.equal(a, b)
