@@ -17,10 +17,13 @@
 //
 // Greedy: one workgroup per (node, sequence) takes the target's argmax of
 // that node (first maximum), then the last workgroup of the sequence walks
-// the tree.  Rejection sampling: one workgroup per sequence, since the walk is
-// sequential by nature; each step is a block-wide pass over the vocabulary.
-// Probabilities are fp64 so that the accept/reject decisions and the sampled
-// token agree with an fp64 reference except in ties at the 1e-12 level.
+// the tree.  Rejection sampling: the walk is sequential by nature, so one
+// workgroup per sequence walks; for vocabularies up to 32768 entries the
+// root's p and every depth's q are first computed in parallel over (row,
+// sequence) and the walk keeps p in registers, otherwise each step is a
+// block-wide pass over the vocabulary in the workspace.  Probabilities are
+// fp64 so that the accept/reject decisions and the sampled token agree with
+// an fp64 reference except in ties at the 1e-12 level.
 #include "internal.h"
 
 using namespace medusa;

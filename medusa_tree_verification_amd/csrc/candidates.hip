@@ -16,11 +16,12 @@
 //      8 (logit, column) pairs under that order; the chunk's top-kmax is then
 //      popped from the 64 lane lists by kmax wave-wide arg-max rounds and
 //      written as a sorted (logit, column) list;
-//   2. one wave per (sequence, head): the chunk lists (in column order) go
-//      into per-lane lists the same way (with at most 64 chunks each lane's
-//      chunk list already is its sorted list), k_d arg-max rounds pop the head's
-//      candidates, and the same wave writes them, the tree tokens of the
-//      nodes at depth head+1, and (head 0) the root and every position.
+//   2. one wave per (sequence, head): with at most 64 chunks each lane's
+//      chunk list already is its sorted list (more chunks are merged into
+//      per-lane lists by sorted insertion, in column order); k_d arg-max
+//      rounds pop the head's candidates, and the same wave writes them, the
+//      tree tokens of the nodes at depth head+1, and (head 0) the root and
+//      every position.
 // The chunk lists live in the caller's workspace.
 #include "internal.h"
 
