@@ -16,7 +16,7 @@
 //   roles that meet at one barrier per 64-key block:
 //   - 4 staging waves stream the split's K/V through buffer loads into
 //     registers, NREG blocks ahead of use, and write each block into one of
-//     two LDS slots: K rows of 256 bytes with their 16-byte chunks
+//     three LDS slots: K rows of 256 bytes with their 16-byte chunks
 //     XOR-swizzled by the row; V transposed (rows = d, 128 bytes) with the 8
 //     keys a lane feeds to one P.V MFMA k-step in one 16-byte granule,
 //     granules XOR-swizzled by a function of d.  Memory stalls of these
@@ -81,7 +81,7 @@ constexpr int MAX_SPLITS = 64;
 // exponents may exceed the reference by up to this much (log2 units), so
 // unnormalised probabilities stay <= 256
 constexpr float RESCALE_SLACK = 8.0f;
-constexpr int LDS_MAX = 160 * 1024;         // LDS of one CU              // the merge keeps one split per lane
+constexpr int LDS_MAX = 160 * 1024;         // LDS of one CU
 constexpr int RSRC_WORD3 = 0x00020000;      // raw buffer, 32-bit data format
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -260,8 +260,9 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
   // split's end reads zeros through its empty buffer resource), and this
   // path never joins the compute waves' code, so the loads in flight are the
   // same on every path and each wait covers exactly the block it needs.
-  // Pipeline: while the compute waves work on block i from its LDS slot,
-  // these waves write block i+1 (from registers) into the other slot and
+  // Pipeline: while the compute waves work on block i (and the second-half
+  // waves finish block i-1) from their LDS slots, these waves write block
+  // i+1 (from registers) into the third slot, the one block i-2 held, and
   // refill those registers with block i+1+NREG.  A slot is rewritten only
   // after the barrier that follows its last reader.  Both roles pass the
   // same number of barriers.
