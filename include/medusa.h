@@ -144,7 +144,7 @@ int medusa_tree_info(const medusa_tree_t* tree, int32_t* T, int32_t* K, int32_t*
  *   logits  [M][K][V] fp32 (output)
  * For dt = MEDUSA_BF16 the residual output r is rounded to bf16 (round to
  * nearest even) before the vocab projection; accumulation is fp32.
- * Constraints: M >= 1, K in 1..MEDUSA_MAX_HEADS, H % 8 == 0 (bf16) ,
+ * Constraints: M >= 1, K in 1..MEDUSA_MAX_HEADS, H % 8 == 0 (bf16),
  * V >= 1, w1_head_stride >= H*H (or 0 only if K == 1), wlm_head_stride == 0
  * or >= V*H.  Pointers 16-byte aligned.
  * Workspace: holds r, K*M*H elements of dt.
@@ -241,6 +241,8 @@ int medusa_tree_candidates(const float* head_logits, const int32_t* root,
  * scores, sums and accumulators; bf16 operands use MFMA.
  * Constraints: Hq % Hkv == 0; D = 128 (bf16) or D <= 128, D % 4 == 0 (f32);
  * T = the tree's T; S_cap >= ctx_max + T.  Pointers 16-byte aligned.
+ * MEDUSA_EUNSUPPORTED when a grid would pass 2^32 work-items (bf16: about
+ * 5.5 million (layer, sequence, K/V head) work items).
  * Workspace: the split partials (every query row's output over one key
  * split, normalised by its own exp-sum, in bf16, plus that split's max and
  * exp-sum in fp32), merged by a second kernel on the same stream; 0 bytes

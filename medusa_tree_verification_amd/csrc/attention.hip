@@ -563,10 +563,10 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
 // O_s the split's normalised output.  Two rows per wave, 32 lanes per row,
 // 4 consecutive d per lane; every split's (max, sum) and output values are
 // requested before any arithmetic (one round trip).
-__global__ __launch_bounds__(256) void merge_splits(AttnArgs a) {
+__global__ __launch_bounds__(64) void merge_splits(AttnArgs a) {
   const int lane = threadIdx.x & 31;  // lane within the row's half-wave
   const int BH = a.B * a.Hkv;
-  const int64_t gr = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int64_t gr = static_cast<int64_t>(blockIdx.x) * 2 + (threadIdx.x >> 5);
   const bool live = gr < static_cast<int64_t>(a.L) * BH * a.QR;  // both halves reach the shuffles
   const int64_t grc = live ? gr : 0;
   const int lbh = static_cast<int>(grc / a.QR);  // = layer * B * Hkv + bh
@@ -876,7 +876,16 @@ int attention_launch(const void* q, const void* k_cache, const void* v_cache, in
   a.QC = p.QC;
   a.NS = p.NS;
   a.chunk = p.chunk;
-  a.tasks = L * B * Hkv * p.QC * p.NS;
+  // both grids must stay within 2^32 work-items (768 per attention
+  // workgroup, 32 per merged row)
+  const int64_t tasks = static_cast<int64_t>(L) * B * Hkv * p.QC * p.NS;
+  const int64_t merge_rows = static_cast<int64_t>(L) * B * Hkv * p.QR;
+  if ((tasks + 7) / 8 * 8 * 768 >= (1ll << 32) || (p.NS > 1 && merge_rows * 32 >= (1ll << 32))) {
+    set_error("tree attention grid too large (L*B*Hkv=%lld, %d splits)",
+              static_cast<long long>(L) * B * Hkv, p.NS);
+    return MEDUSA_EUNSUPPORTED;
+  }
+  a.tasks = static_cast<int>(tasks);
   a.per_xcd = (a.tasks + 7) / 8;
   a.scale_log2 = scale * LOG2E;
   a.out = static_cast<uint16_t*>(out);
@@ -895,7 +904,8 @@ int attention_launch(const void* q, const void* k_cache, const void* v_cache, in
   }
   if (rc || p.NS == 1) return rc;
   const int64_t rows = static_cast<int64_t>(L) * B * Hkv * p.QR;
-  hipLaunchKernelGGL(merge_splits, dim3(static_cast<unsigned>((rows + 7) / 8)), dim3(256), 0, stream, a);
+  // one wave (two rows) per workgroup: measured faster than 4 or 16 waves
+  hipLaunchKernelGGL(merge_splits, dim3(static_cast<unsigned>((rows + 1) / 2)), dim3(64), 0, stream, a);
   return check_launch("tree attention split merge");
 }
 
