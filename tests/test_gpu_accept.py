@@ -18,11 +18,12 @@ DEV = "cuda"
 TIE = 1e-9
 
 
-def _compare(w, parent, rank, tau, seed_extra, plant=True, tree_tokens=None):
+def _compare(w, parent, rank, tau, seed_extra, plant=True, tree_tokens=None, inputs=None):
     t = api.Tree(parent, rank, w.topk)
     toks = synth.tree_tokens_input(w, parent, seed_extra) if tree_tokens is None else tree_tokens
-    base, head, ua, us = synth.accept_inputs(w, parent, toks, "cpu", plant=plant,
-                                             seed_extra=seed_extra)
+    if inputs is None:
+        inputs = synth.accept_inputs(w, parent, toks, "cpu", plant=plant, seed_extra=seed_extra)
+    base, head, ua, us = inputs
     announce("accept", w.name, "tau", tau, "seed", seed_extra)
     acc, otok, onode = api.accept_paths(base.to(DEV), head.to(DEV),
                                         torch.from_numpy(toks).to(DEV), t, ua.to(DEV), us.to(DEV),
@@ -32,6 +33,7 @@ def _compare(w, parent, rank, tau, seed_extra, plant=True, tree_tokens=None):
                                                      rank, ua.numpy(), us.numpy(),
                                                      float(np.float32(tau)), w.K)
     g_acc, g_tok, g_node = acc.cpu().numpy(), otok.cpu().numpy(), onode.cpu().numpy()
+    _compare.last_gpu = g_acc
     for b in range(w.B):
         same = (g_acc[b] == r_acc[b] and np.array_equal(g_tok[b], r_tok[b])
                 and np.array_equal(g_node[b], r_node[b]))
@@ -153,3 +155,43 @@ def test_accept_rejection_clamps_out_of_range_tokens():
         torch.cuda.synchronize()
         for a, b in zip(r_bad, r_good):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("V", [1024, 40000])
+def test_accept_rejection_degenerate_distributions(V):
+    """Two degenerate cases of the acceptance rule, both sizes of the
+    distribution path, against the oracle:
+    - p = q at every node (each node's target logits equal the head logits
+      its children were drafted from): the ratio is 1, every first child is
+      accepted, and each walk follows the rank-0 children down to a leaf;
+    - the target gives every drafted token probability 0 (its logit far
+      below the rest, so exp underflows in fp64): every child is rejected,
+      and the emitted token comes from the residual max(0, p - q) / Z at the
+      root."""
+    w = synth.WORKLOADS["tiny-fp32"].scaled(B=3, V=V, K=3, topk=(4, 3, 2), T=14, cfg_id=495)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    depth = synth.depths_of(parent)
+    toks = synth.tree_tokens_input(w, parent, 3)
+    base, head, ua, us = synth.accept_inputs(w, parent, toks, "cpu", plant=False, seed_extra=3)
+    kids = {}
+    for n in range(1, w.T):
+        kids.setdefault(int(parent[n]), []).append(n)
+    # the rank-0 chain from the root
+    u, chain_depth = 0, 0
+    while u in kids:
+        u = min(kids[u], key=lambda c: rank[c])
+        chain_depth += 1
+
+    same = base.clone()
+    for n in range(w.T):
+        if depth[n] < w.K:
+            same[:, n] = head[:, depth[n]]
+    r_acc = _compare(w, parent, rank, 0.7, 3, tree_tokens=toks, inputs=(same, head, ua, us))
+    assert (r_acc == chain_depth).all() and (_compare.last_gpu == chain_depth).all()
+
+    zero = base.clone()
+    for b in range(w.B):
+        for n in range(1, w.T):
+            zero[b, int(parent[n]), int(toks[b, n])] = -1.0e4
+    r_acc = _compare(w, parent, rank, 0.7, 3, tree_tokens=toks, inputs=(zero, head, ua, us))
+    assert (r_acc == 0).all() and (_compare.last_gpu == 0).all()
