@@ -68,6 +68,9 @@ __global__ __launch_bounds__(GT) void accept_greedy_kernel(AcceptArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   __shared__ float s_v[GT / 64];
   __shared__ int s_i[GT / 64];
+  __shared__ int s_last;
+  __shared__ int32_t s_am[MEDUSA_MAX_TREE_NODES], s_tk[MEDUSA_MAX_TREE_NODES];
+  __shared__ int32_t s_cs[MEDUSA_MAX_TREE_NODES + 1], s_cl[MEDUSA_MAX_TREE_NODES];
   const float* row = a.base + (static_cast<int64_t>(b) * a.T + n) * a.V;
   float bv = -INFINITY;
   int bi = -1;
@@ -117,32 +120,48 @@ __global__ __launch_bounds__(GT) void accept_greedy_kernel(AcceptArgs a) {
     s_i[wave] = bi;
   }
   __syncthreads();
-  if (tid != 0) return;  // the rest is one thread's work
-  float wv = s_v[0];
-  int wi = s_i[0];
-  for (int w = 1; w < GT / 64; ++w)
-    if (beats(s_v[w], s_i[w], wv, wi)) {
-      wv = s_v[w];
-      wi = s_i[w];
+  if (tid == 0) {
+    float wv = s_v[0];
+    int wi = s_i[0];
+    for (int w = 1; w < GT / 64; ++w)
+      if (beats(s_v[w], s_i[w], wv, wi)) {
+        wv = s_v[w];
+        wi = s_i[w];
+      }
+    a.argmax[static_cast<int64_t>(b) * a.T + n] = wi;
+    __threadfence();  // the argmax is visible device-wide before the count
+    const int last = atomicAdd(a.counters + b, 1) == a.T - 1;
+    if (last) {
+      __threadfence();  // every node's argmax is visible from here on
+      a.counters[b] = 0;  // ready for the next call
     }
-  a.argmax[static_cast<int64_t>(b) * a.T + n] = wi;
-  __threadfence();  // the argmax is visible device-wide before the count
-  const int old = atomicAdd(a.counters + b, 1);
-  if (old != a.T - 1) return;
-  __threadfence();  // every node's argmax is visible from here on
-  a.counters[b] = 0;  // ready for the next call
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;  // the whole workgroup
+  // the last workgroup of the sequence: every node's argmax and token and
+  // the child lists go to LDS in one parallel round trip, then one thread
+  // walks the tree there
   const int32_t* am = a.argmax + static_cast<int64_t>(b) * a.T;
   const int32_t* tk = a.toks + static_cast<int64_t>(b) * a.T;
+  if (tid < a.T) {
+    s_am[tid] = am[tid];
+    s_tk[tid] = tk[tid];
+  }
+  if (tid <= a.T) s_cs[tid] = a.child_start[tid];
+  if (tid < a.T - 1) s_cl[tid] = a.child_list[tid];
+  __syncthreads();
+  if (tid != 0) return;
   int32_t* onodes = a.out_nodes + static_cast<int64_t>(b) * a.Kp1;
   int32_t* otoks = a.out_tokens + static_cast<int64_t>(b) * a.Kp1;
   int u = 0, len = 0;
   while (true) {
     onodes[len] = u;
-    const int t = am[u];
+    const int t = s_am[u];
     int nxt = -1;
-    for (int ci = a.child_start[u]; ci < a.child_start[u + 1]; ++ci) {
-      const int c = a.child_list[ci];
-      if (tk[c] == t) {
+    for (int ci = s_cs[u]; ci < s_cs[u + 1]; ++ci) {
+      const int c = s_cl[ci];
+      if (s_tk[c] == t) {
         nxt = c;
         break;
       }
@@ -151,7 +170,7 @@ __global__ __launch_bounds__(GT) void accept_greedy_kernel(AcceptArgs a) {
       otoks[len] = t;
       break;
     }
-    otoks[len] = tk[nxt];
+    otoks[len] = s_tk[nxt];
     ++len;
     u = nxt;
   }
