@@ -3,6 +3,10 @@ infrastructure only): heads -> per-head top-k -> tree tokens/positions ->
 tree attention per layer -> acceptance.  The base model itself (which turns
 the attention outputs into the verification logits) is not part of the path:
 its logits are an input, as are the per-layer Q/K/V.
+Pinned on inputs with a closed-form outcome: W1 = 0 and a one-hot hidden
+state give every head a prescribed logit order (so the top-k and tree tokens
+are known), identical V rows fix every attention output, and planted greedy
+argmaxes fix the accepted path.
 """
 from __future__ import annotations
 

@@ -1,0 +1,114 @@
+"""One whole verify step through the C ABI (heads, candidates, every layer's
+tree attention, acceptance), as the benchmark runs it, against the oracle.
+
+Continuous outputs (head logits, attention) are compared with the oracle's
+own fp64 chain within the dtype's tolerance.  Discrete outputs (top-k, tree
+tokens, positions, the accepted path) must equal the oracle's decisions taken
+on the values the GPU computed upstream (identical logits give identical
+decisions; rejection sampling decides in fp64 on both sides, so only a
+decision margin below 1e-9 may differ).  For the fp32 configuration the
+oracle's composed step is also compared as a whole, after checking that its
+selection gaps are far above the fp32 error."""
+import numpy as np
+import pytest
+import torch
+
+from medusa_tree_verification_amd import api, synth
+from oracle import accept as oaccept
+from oracle import heads as oheads
+from oracle import step as ostep
+from oracle import topk as otopk
+from oracle import tree as otree
+from oracle import attention as oattn
+from helpers import TOL_BF16, TOL_F32, announce, row_rel_err, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TIE = 1e-9
+
+CASES = {
+    "tiny-fp32": synth.WORKLOADS["tiny-fp32"].scaled(B=3, L=2, cfg_id=520),
+    "bf16-small": synth.WORKLOADS["vicuna7b-shaped"].scaled(B=2, H=256, V=2000, L=2, Hq=8, Hkv=4,
+                                                            ctx=300, cfg_id=521),
+}
+
+
+def _gpu_step(w, tree, tau, parent):
+    hidden, w1, wlm = synth.head_inputs(w, DEV)
+    root = synth.roots(w, DEV)
+    layers = [synth.attention_inputs(w, l, DEV)[:3] for l in range(w.L)]
+    ctx = torch.full((w.B,), w.ctx, dtype=torch.int32, device=DEV)
+    logits = api.heads(hidden, w1, wlm)
+    topk, toks, pos = api.tree_candidates(logits, root, ctx, tree)
+    outs = [api.tree_attention(q, k, v, ctx, w.ctx, tree) for (q, k, v) in layers]
+    torch.cuda.synchronize()
+    base, _, ua, us = synth.accept_inputs(w, parent, toks.cpu().numpy(), "cpu", plant=True, seed_extra=4)
+    acc = api.accept_paths(base.to(DEV), logits if tau > 0 else None, toks, tree,
+                           ua.to(DEV), us.to(DEV), tau)
+    torch.cuda.synchronize()
+    return dict(hidden=hidden, w1=w1, wlm=wlm, root=root, layers=layers, logits=logits, topk=topk,
+                toks=toks, pos=pos, outs=outs, base=base, ua=ua, us=us, acc=acc)
+
+
+def _same_path(g, r, res):
+    """GPU and oracle accepted paths agree, or differ only where the oracle's
+    own decision margin is a tie."""
+    g_acc, g_tok, g_node = (x.cpu().numpy() for x in g)
+    r_acc, r_tok, r_node = r
+    for b in range(len(r_acc)):
+        same = (g_acc[b] == r_acc[b] and np.array_equal(g_tok[b], r_tok[b])
+                and np.array_equal(g_node[b], r_node[b]))
+        if not same:
+            margins = [m for (_, _, m) in res[b].trace]
+            assert min(margins, default=1.0) < TIE, (b, g_acc[b], r_acc[b])
+
+
+@pytest.mark.parametrize("name,tau", [("tiny-fp32", 0.0), ("tiny-fp32", 1.0),
+                                      ("bf16-small", 0.0), ("bf16-small", 0.7)])
+def test_verify_step_against_oracle(name, tau):
+    w = CASES[name]
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    tree = api.Tree(parent, rank, w.topk)
+    announce("verify step", name, "tau", tau)
+    g = _gpu_step(w, tree, tau, parent)
+    bf16 = w.dtype == "bf16"
+    tol = TOL_BF16 if bf16 else TOL_F32
+    vis = otree.visible_bruteforce(parent)
+    ctx_np = np.full(w.B, w.ctx)
+    # continuous outputs against the fp64 chain
+    ref_logits = oheads.medusa_heads(to64(g["hidden"]), to64(g["w1"]), to64(g["wlm"]), round_r=bf16)
+    g_logits = g["logits"].cpu().numpy()
+    assert row_rel_err(g_logits.reshape(-1, w.V), ref_logits.reshape(-1, w.V)) <= tol
+    for (q, k, v), o in zip(g["layers"], g["outs"]):
+        ref = oattn.tree_attention(to64(q), to64(k), to64(v), ctx_np, vis)
+        assert row_rel_err(to64(o).reshape(-1, w.D), ref.reshape(-1, w.D)) <= tol
+    # discrete outputs: the oracle's decisions on the GPU's upstream values
+    r_topk = otopk.head_topk(g_logits, list(w.topk))
+    assert (g["topk"].cpu().numpy() == r_topk).all()
+    r_toks = otree.tree_tokens(r_topk, g["root"].cpu().numpy(), parent, rank)
+    assert (g["toks"].cpu().numpy() == r_toks).all()
+    assert (g["pos"].cpu().numpy() == otree.positions(ctx_np, parent)).all()
+    r_acc, r_tok, r_node, res = oaccept.accept_paths(g["base"].numpy(), g_logits, r_toks, parent, rank,
+                                                     g["ua"].numpy(), g["us"].numpy(),
+                                                     float(np.float32(tau)), w.K)
+    _same_path(g["acc"], (r_acc, r_tok, r_node), res)
+    if bf16:
+        return
+    # fp32: the oracle's whole composed step, its top-k gaps far above the error
+    srt = -np.sort(-ref_logits, axis=-1)
+    kmax = max(w.topk)
+    gap = np.min(srt[..., :kmax] - srt[..., 1:kmax + 1])
+    assert gap > 10 * TOL_F32 * np.max(np.abs(ref_logits)), gap
+    whole = ostep.verify_step(to64(g["hidden"]), to64(g["w1"]), to64(g["wlm"]), False,
+                              g["root"].cpu().numpy(), ctx_np, parent, rank, list(w.topk),
+                              [tuple(to64(x) for x in lay) for lay in g["layers"]],
+                              g["base"].numpy(), g["ua"].numpy(), g["us"].numpy(),
+                              float(np.float32(tau)))
+    assert (whole["topk"] == g["topk"].cpu().numpy()).all()
+    assert (whole["tree_tokens"] == g["toks"].cpu().numpy()).all()
+    for o, ref in zip(g["outs"], whole["attn"]):
+        assert row_rel_err(to64(o).reshape(-1, w.D), ref.reshape(-1, w.D)) <= tol
+    _same_path(g["acc"], (whole["accept_len"], whole["out_tokens"], whole["out_nodes"]),
+               oaccept.accept_paths(g["base"].numpy(), whole["head_logits"], whole["tree_tokens"],
+                                    parent, rank, g["ua"].numpy(), g["us"].numpy(),
+                                    float(np.float32(tau)), w.K)[3])
