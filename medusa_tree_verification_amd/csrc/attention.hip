@@ -101,7 +101,7 @@ struct AttnArgs {
   float scale_log2;
   uint16_t* out;
   uint16_t* part_o;  // [NS][B*Hkv][QRpad][D] bf16, normalised (O / sum)
-  float* part_ml;    // [NS][B*Hkv][QRpad][2] fp32 (max, sum)
+  float* part_ml;    // [B*Hkv][QRpad][NS][2] fp32 (max, sum): a row's splits side by side
   int lds_mask, lds_q, lds_ring;  // dynamic LDS layout (byte offsets)
 };
 
@@ -553,7 +553,9 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
         const f32x4 v = o[t][dt] * inv;
         *reinterpret_cast<uint2*>(po + dt * 16 + 4 * grp) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
       }
-      if (grp == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_run[t], l_run[t]);
+      if (grp == 0)
+        *reinterpret_cast<float2*>(a.part_ml + ((static_cast<int64_t>(lbh) * a.QRpad + r) * a.NS + split) * 2) =
+            make_float2(m_run[t], l_run[t]);
     }
   }
 }
@@ -577,8 +579,8 @@ __global__ __launch_bounds__(64) void merge_splits(AttnArgs a) {
   const int ns = a.NS;
   // lane s holds splits s and s + 32
   float2 ml0 = make_float2(-INFINITY, 0.f), ml1 = make_float2(-INFINITY, 0.f);
-  if (lane < ns) ml0 = *reinterpret_cast<const float2*>(a.part_ml + (lane * stride + row) * 2);
-  if (lane + 32 < ns) ml1 = *reinterpret_cast<const float2*>(a.part_ml + ((lane + 32) * stride + row) * 2);
+  if (lane < ns) ml0 = *reinterpret_cast<const float2*>(a.part_ml + (row * ns + lane) * 2);
+  if (lane + 32 < ns) ml1 = *reinterpret_cast<const float2*>(a.part_ml + (row * ns + lane + 32) * 2);
   uint2 ov[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u)
