@@ -243,6 +243,12 @@ int medusa_tree_candidates(const float* head_logits, const int32_t* root,
  * T = the tree's T; S_cap >= ctx_max + T.  Pointers 16-byte aligned.
  * MEDUSA_EUNSUPPORTED when a grid would pass 2^32 work-items (bf16: about
  * 5.5 million (layer, sequence, K/V head) work items).
+ * Split count: chosen per call from the shape and the device (the most
+ * splits whose workgroups run in one round of the resident slots).  The
+ * environment variable MEDUSA_ATTN_SPLITS = n > 0 (read by every call, the
+ * workspace-size calls included, so set it before sizing) asks for n splits
+ * instead (at most 64, at least one 64-key block each); results agree with
+ * the default within rounding.  Meant for tests and tuning.
  * Workspace: the split partials (every query row's output over one key
  * split, normalised by its own exp-sum, in bf16, plus that split's max and
  * exp-sum in fp32), merged by a second kernel on the same stream; 0 bytes
