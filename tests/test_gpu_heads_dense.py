@@ -170,3 +170,22 @@ def test_dense_heavy_ties(M):
     torch.cuda.synchronize()
     assert (idx[:, 0].cpu().numpy() == np.arange(10)).all()
     _check(hidden, w1, wlm, t, (10, 10), TOL_BF16, round_r=True)
+
+
+def test_dense_deterministic():
+    """Two calls on the same inputs give identical indices, values and
+    logits, on both tile shapes (M = 64 and M = 256)."""
+    for M in (64, 256):
+        w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=1, H=256, V=3000, K=3, topk=(10, 5, 3), T=16,
+                                                      cfg_id=460 + M)
+        hidden, w1, wlm = synth.head_inputs(w, DEV, M=M)
+        t = _tree((10, 5, 3), 16)
+        announce("dense heads determinism", M)
+        runs = []
+        for _ in range(2):
+            logits = torch.empty((M, 3, 3000), dtype=torch.float32, device=DEV)
+            idx, val = api.heads_dense(hidden, w1, wlm, t, logits=logits)
+            runs.append((idx, val, logits))
+        torch.cuda.synchronize()
+        for a, b in zip(*runs):
+            assert torch.equal(a, b)
