@@ -116,7 +116,7 @@ def test_dense_ties_go_to_the_lower_index():
     assert (idx.cpu().numpy() == otopk.head_topk(lg, [6])).all()
 
 
-@pytest.mark.parametrize("name", ["vicuna7b-shaped", "zephyr7b-shaped"])
+@pytest.mark.parametrize("name", ["vicuna7b-shaped", "vicuna13b-shaped", "vicuna33b-shaped", "zephyr7b-shaped"])
 def test_dense_full_size(name):
     """M = B*T rows at the workload's shape; the oracle recomputes sampled
     (row, head) logit rows in full."""
