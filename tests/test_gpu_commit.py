@@ -139,3 +139,46 @@ def test_multistep_greedy_loop_on_device():
         ev = torch.from_numpy(ev).to(torch.bfloat16).float().numpy()
         np.testing.assert_array_equal(kf[:, b, :, : final_ctx[b]], ek)
         np.testing.assert_array_equal(vf[:, b, :, : final_ctx[b]], ev)
+
+
+@pytest.mark.parametrize("name", ["vicuna7b-shaped", "zephyr7b-shaped"])
+def test_commit_full_size(name):
+    """Every layer of a workload's caches at full size: after the commit, slot
+    ctx + d of every (layer, sequence, K/V head) holds what slot
+    ctx + node_d held before (d = 1 .. accept_len), and every other slot is
+    unchanged -- the definition of the move, checked on the device for all
+    rows (the caches are too large to copy to the host oracle)."""
+    w = synth.WORKLOADS[name]
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    t = api.Tree(parent, rank, w.topk)
+    kids = otree.children_in_rank_order(parent, rank)
+    rng = np.random.default_rng(77)
+    S_cap = w.ctx + w.T
+    ctx = [w.ctx - int(x) for x in rng.integers(0, 5, w.B)]
+    shape = (w.L, w.B, w.Hkv, S_cap, w.D)
+    k0 = torch.randn(shape, dtype=torch.float32, device=DEV).to(torch.bfloat16)
+    v0 = torch.randn(shape, dtype=torch.float32, device=DEV).to(torch.bfloat16)
+    k, v = k0.clone(), v0.clone()
+    acc, nodes, out = [], np.full((w.B, w.K + 1), -1), np.full((w.B, w.K + 1), -1)
+    for b in range(w.B):
+        path, u = [0], 0
+        while kids[u] and len(path) <= w.K - b % w.K:    # sequence 0 goes to full depth
+            u = int(rng.choice(kids[u]))
+            path.append(u)
+        acc.append(len(path) - 1)
+        nodes[b, : len(path)] = path
+        out[b, : len(path)] = rng.integers(0, w.V, len(path))
+    i32 = lambda x: torch.tensor(np.asarray(x), dtype=torch.int32, device=DEV)
+    announce("commit full size", name, acc)
+    cn, rn = api.commit_accepted(k, v, i32(acc), i32(nodes), i32(out), i32(ctx), t)
+    torch.cuda.synchronize()
+    expect_k, expect_v = k0.clone(), v0.clone()
+    for b in range(w.B):
+        for d in range(1, acc[b] + 1):
+            expect_k[:, b, :, ctx[b] + d] = k0[:, b, :, ctx[b] + nodes[b, d]]
+            expect_v[:, b, :, ctx[b] + d] = v0[:, b, :, ctx[b] + nodes[b, d]]
+    assert torch.equal(k, expect_k) and torch.equal(v, expect_v)
+    assert cn.tolist() == [ctx[b] + acc[b] + 1 for b in range(w.B)]
+    assert rn.tolist() == [int(out[b, acc[b]]) for b in range(w.B)]
+    del k0, v0, k, v, expect_k, expect_v
+    torch.cuda.empty_cache()
