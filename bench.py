@@ -142,7 +142,7 @@ def build_step(w, dev):
                       torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev))
                 for tau in w.temperature}
 
-    def ws(n):  # zero-filled: some workspaces hold arrival counters
+    def ws(n):
         return torch.zeros(max(n, 256), dtype=torch.uint8, device=dev)
 
     ws_heads = ws(api.heads_workspace_size(w.B, w.H, w.K, torch.bfloat16))

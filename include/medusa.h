@@ -38,9 +38,8 @@
  *     same thread).  No exception crosses the ABI.
  *   - Scratch memory is passed in by the caller (ws, ws_bytes, sized by the
  *     matching *_workspace_size call, 256-byte aligned).  No call allocates
- *     device memory except medusa_tree_create.  The workspace of greedy
- *     medusa_accept_paths holds arrival counters: zero-fill it once before
- *     its first use; every call leaves it zero-filled again.
+ *     device memory except medusa_tree_create, and no workspace needs
+ *     initialising.
  *   - Floating-point inputs must be finite.  Non-finite inputs give
  *     unspecified outputs, but every kernel still terminates and every index
  *     written stays in its documented range (or -1).
@@ -313,12 +312,12 @@ int medusa_tree_attention_layers(const void* q, const void* k_cache, const void*
  *   accept_len  [B] int32 (output) number of accepted tree nodes, 0..max depth
  *   out_tokens  [B][K+1] int32 (output) accept_len + 1 emitted tokens, -1 after
  *   out_nodes   [B][K+1] int32 (output) root (0) then the accepted nodes, -1 after
- * Workspace: greedy keeps each node's argmax and one arrival counter per
- * sequence (zero-filled before first use); rejection sampling keeps one fp64
+ * Workspace: greedy keeps each node's argmax (a first kernel computes them
+ * in parallel, a second walks the tree); rejection sampling keeps one fp64
  * distribution per sequence and, for V <= 32768, also the root's p and each
  * depth's q (fp64, max_depth + 1 rows per sequence) computed in parallel
- * before the walk, which then holds p in registers.  Rejection-sampling
- * workspaces need no initialisation.
+ * before the walk, which then holds p in registers.  No initialisation is
+ * needed; calls that share a workspace must not overlap.
  * ------------------------------------------------------------------------ */
 size_t medusa_accept_workspace_size(int B, int V, const medusa_tree_t* tree,
                                     float temperature);

@@ -110,8 +110,8 @@ class Tree:
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
-    """A caller's workspace, or a new zero-filled one (the greedy acceptance
-    workspace holds arrival counters that must start at zero)."""
+    """A caller's workspace, or a new one (zero-filled, though no call needs
+    that)."""
     if ws is None:
         if nbytes == 0:
             return None, 0

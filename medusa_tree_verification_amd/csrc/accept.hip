@@ -51,13 +51,13 @@ struct AcceptArgs {
   double* pbuf;        // [B][V]       (rejection)
   double* qbuf;        // [B][max_depth + 1][V] (rejection, V <= RT * 32): row 0 the root's p, row d q_d
   int32_t* argmax;     // [B][T]       (greedy)
-  int* counters;       // [B], zero between calls (greedy)
 };
 
 // ---------------------------------------------------------------------------
 // greedy: the target's argmax of every tree node in parallel (one workgroup
-// per node and sequence, the whole row in flight at once), then the last
-// workgroup of a sequence to finish walks the tree over those argmaxes.
+// per node and sequence, the whole row in flight at once), then a second
+// launch walks each sequence's tree over those argmaxes (a second launch
+// costs less than publishing the argmaxes device-wide from every workgroup).
 // ---------------------------------------------------------------------------
 constexpr int GT = 1024;
 
@@ -68,9 +68,6 @@ __global__ __launch_bounds__(GT) void accept_greedy_kernel(AcceptArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   __shared__ float s_v[GT / 64];
   __shared__ int s_i[GT / 64];
-  __shared__ int s_last;
-  __shared__ int32_t s_am[MEDUSA_MAX_TREE_NODES], s_tk[MEDUSA_MAX_TREE_NODES];
-  __shared__ int32_t s_cs[MEDUSA_MAX_TREE_NODES + 1], s_cl[MEDUSA_MAX_TREE_NODES];
   const float* row = a.base + (static_cast<int64_t>(b) * a.T + n) * a.V;
   float bv = -INFINITY;
   int bi = -1;
@@ -129,27 +126,29 @@ __global__ __launch_bounds__(GT) void accept_greedy_kernel(AcceptArgs a) {
         wi = s_i[w];
       }
     a.argmax[static_cast<int64_t>(b) * a.T + n] = wi;
-    __threadfence();  // the argmax is visible device-wide before the count
-    const int last = atomicAdd(a.counters + b, 1) == a.T - 1;
-    if (last) {
-      __threadfence();  // every node's argmax is visible from here on
-      a.counters[b] = 0;  // ready for the next call
-    }
-    s_last = last;
   }
-  __syncthreads();
-  if (!s_last) return;  // the whole workgroup
-  // the last workgroup of the sequence: every node's argmax and token and
-  // the child lists go to LDS in one parallel round trip, then one thread
-  // walks the tree there
+}
+
+// The walk, one workgroup per sequence: every node's argmax and token and
+// the child lists go to LDS in one parallel round trip, then one thread
+// walks the tree there.
+constexpr int GW = 256;  // >= MEDUSA_MAX_TREE_NODES + 1
+
+__global__ __launch_bounds__(GW) void accept_greedy_walk(AcceptArgs a) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ int32_t s_am[MEDUSA_MAX_TREE_NODES], s_tk[MEDUSA_MAX_TREE_NODES];
+  __shared__ int32_t s_cs[MEDUSA_MAX_TREE_NODES + 1], s_cl[MEDUSA_MAX_TREE_NODES];
   const int32_t* am = a.argmax + static_cast<int64_t>(b) * a.T;
   const int32_t* tk = a.toks + static_cast<int64_t>(b) * a.T;
-  if (tid < a.T) {
-    s_am[tid] = am[tid];
-    s_tk[tid] = tk[tid];
+  for (int i = tid; i <= a.T; i += GW) {
+    if (i < a.T) {
+      s_am[i] = am[i];
+      s_tk[i] = tk[i];
+    }
+    s_cs[i] = a.child_start[i];
+    if (i < a.T - 1) s_cl[i] = a.child_list[i];
   }
-  if (tid <= a.T) s_cs[tid] = a.child_start[tid];
-  if (tid < a.T - 1) s_cl[tid] = a.child_list[tid];
   __syncthreads();
   if (tid != 0) return;
   int32_t* onodes = a.out_nodes + static_cast<int64_t>(b) * a.Kp1;
@@ -626,7 +625,7 @@ extern "C" size_t medusa_accept_workspace_size(int B, int V, const medusa_tree_t
                                                float temperature) {
   if (B < 1 || V < 1 || !tree) return 0;
   if (temperature == 0.f)
-    return round_up(static_cast<size_t>(B) * tree->T * 4, 256) + round_up(static_cast<size_t>(B) * 4, 256);
+    return round_up(static_cast<size_t>(B) * tree->T * 4, 256);
   size_t n = round_up(static_cast<size_t>(B) * V * sizeof(double), 256);
   if (reject_per(V)) n += round_up(static_cast<size_t>(B) * (tree->max_depth + 1) * V * sizeof(double), 256);
   return n;
@@ -675,10 +674,11 @@ extern "C" int medusa_accept_paths(const float* base_logits, const float* head_l
   }
   if (temperature == 0.f) {
     a.argmax = static_cast<int32_t*>(ws);
-    a.counters = reinterpret_cast<int*>(static_cast<char*>(ws) +
-                                        round_up(static_cast<size_t>(B) * tree->T * 4, 256));
     hipLaunchKernelGGL(accept_greedy_kernel, dim3(tree->T, B), dim3(GT), 0, stream, a);
-    return check_launch("greedy acceptance");
+    int rc = check_launch("greedy acceptance (argmax)");
+    if (rc) return rc;
+    hipLaunchKernelGGL(accept_greedy_walk, dim3(B), dim3(GW), 0, stream, a);
+    return check_launch("greedy acceptance (walk)");
   }
   a.pbuf = static_cast<double*>(ws);
   switch (reject_per(V)) {

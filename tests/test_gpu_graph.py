@@ -1,8 +1,8 @@
 """The verify step captured as a HIP graph (as the benchmark runs it):
 several replays, with eager work and synchronisations between them, each
-checked against the eager result.  Attention and greedy acceptance keep
-arrival counters in their workspaces, so replays also check that those
-counters return to zero."""
+checked against the eager result.  The workspaces are reused by every
+replay and eager call, so the replays also check that no call depends on
+what an earlier call left in them."""
 import numpy as np
 import pytest
 import torch
