@@ -65,6 +65,32 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def read_probe(gib: int = 2, reps: int = 5) -> dict:
+    """Read bandwidth of the library's streaming read probe
+    (medusa_read_probe: every 16-byte piece of a buffer larger than the
+    chip's last-level cache read once, coalesced), timed between two events
+    on the launch stream; it sets the roofline's 8 TB/s beside what a
+    streaming kernel reaches on this chip."""
+    import torch
+    from medusa_tree_verification_amd import api
+    n = gib * (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.int32, device="cuda")
+    parts = api.read_probe(x)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        api.read_probe(x, parts)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / reps
+    del x
+    torch.cuda.empty_cache()
+    return {"gbs": round(n * 4 / (us * 1e-6) / 1e9, 1), "bytes": n * 4,
+            "method": f"medusa_read_probe over {gib} GiB, {reps} launches"}
+
+
 def counter_traffic(w, label: str, source: str):
     """HBM bytes per launch measured by the FETCH_SIZE / WRITE_SIZE counter runs
     recorded in profiles/hbm_counters_<workload>.txt (scaled by a plain copy
@@ -417,6 +443,11 @@ def main():
         "stages_us": {k: round(v, 2) for k, v in stages_us.items()},
         "wall_s_timed": round(wall_s, 4),
     }
+    probe = read_probe()
+    probe["tree_attention_frac"] = round(attn_gbs / probe["gbs"], 4)
+    probe["tree_attention_batched_frac"] = round(result["tree_attention_batched"]["hbm_gbs"] / probe["gbs"], 4)
+    probe["heads_frac"] = round(heads_gbs / probe["gbs"], 4)
+    result["hbm_read_probe"] = probe
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_layers)

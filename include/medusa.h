@@ -383,6 +383,23 @@ int medusa_commit_accepted(void* k_cache, void* v_cache, int64_t layer_stride, i
 int medusa_tree_optimize(const double* p_accept, int K, int kmax_in, const int32_t* k_per_depth,
                          int T, int32_t* parent_out, int32_t* rank_out, double* expected_out);
 
+/* ------------------------------------------------------------------------
+ * Diagnostics: read-bandwidth probe
+ *
+ * Not a stage of the method.  A plain streaming read of `bytes` bytes of
+ * device memory (every 16-byte piece once, coalesced, grid-stride), the rate
+ * a streaming kernel reaches on this chip, reported by the benchmark beside
+ * the rooflines' peak.  The pieces are folded by XOR so that none can be
+ * skipped: partials[i] (i < medusa_read_probe_partials()) receives workgroup
+ * i's fold, and the XOR of all partials equals the XOR of every 32-bit word
+ * of the buffer.
+ *   buf       device, 16-byte aligned; bytes a multiple of 16 (0 allowed)
+ *   partials  device, medusa_read_probe_partials() uint32 words (output)
+ * ------------------------------------------------------------------------ */
+int medusa_read_probe_partials(void);
+
+int medusa_read_probe(const void* buf, size_t bytes, uint32_t* partials, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

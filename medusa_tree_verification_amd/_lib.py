@@ -56,6 +56,8 @@ SIGNATURES = {
                                        c_int, c_int, P_void]),
     "medusa_tree_optimize": (c_int, [ctypes.POINTER(ctypes.c_double), c_int, c_int, P_i32, c_int,
                                      P_i32, P_i32, ctypes.POINTER(ctypes.c_double)]),
+    "medusa_read_probe_partials": (c_int, []),
+    "medusa_read_probe": (c_int, [P_void, c_size_t, P_void, P_void]),
 }
 
 _lib = None

@@ -317,3 +317,15 @@ def tree_optimize(p_accept, k_per_depth, T: int):
     _check(lib.medusa_tree_optimize(p.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), K, kmax,
                                     _p32(kpd), T, _p32(parent), _p32(rank), ctypes.byref(e)))
     return parent, rank, e.value
+
+
+def read_probe(buf: torch.Tensor, partials=None, stream=None) -> torch.Tensor:
+    """Diagnostics: streaming read of a device tensor (contiguous, bytes a
+    multiple of 16) -> per-workgroup XOR folds [medusa_read_probe_partials()]
+    uint32 (as int32); their XOR is the XOR of every 32-bit word of buf."""
+    lib = _lib.load()
+    if partials is None:
+        partials = torch.empty(lib.medusa_read_probe_partials(), dtype=torch.int32, device=buf.device)
+    _check(lib.medusa_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(partials),
+                                 _stream(stream)))
+    return partials
