@@ -296,7 +296,10 @@ int medusa_tree_attention_layers(const void* q, const void* k_cache, const void*
  * temperature > 0: rejection sampling.  P1, section "수학적 무손실 보장: 기각
  * 샘플링": a draft x is accepted iff u < min(1, p(x)/q(x)); after a rejection
  * p becomes max(0, p - q) / sum(max(0, p - q)); P3, section 2, shows the
- * output is distributed as p.  On the tree: p_u = softmax(base_logits[b][u]
+ * output is distributed as p when each draft is a sample from q.  Drafts
+ * taken by top-k (as medusa_tree_candidates fills the tree) are not samples
+ * from q, so on such trees that distribution guarantee does not hold; the
+ * call computes the same rule either way.  On the tree: p_u = softmax(base_logits[b][u]
  * / temperature), q_d = softmax(head_logits[b][d-1] / temperature) for a child
  * at depth d; children are tried in rank order with u_accept[b][child]; a
  * rejection turns p into the residual before the next sibling; an accepted

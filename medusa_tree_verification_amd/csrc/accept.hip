@@ -10,10 +10,14 @@
 // 보장: 기각 샘플링": a draft x is accepted iff r < min(1, p(x)/q(x)); after a
 // rejection the target distribution is replaced by the residual
 // max(0, p - q) / sum(max(0, p - q)); P3, section 2, proves the emitted token
-// is distributed as p.  On the tree the children of the current node are
-// tried in rank order (the residual carries over from one sibling to the
-// next), an accepted child becomes the current node, and the walk ends with
-// one token drawn from the current p by inverse CDF.
+// is distributed as p when the draft is a sample from q.  On the tree the
+// children of the current node are tried in rank order (the residual carries
+// over from one sibling to the next), an accepted child becomes the current
+// node, and the walk ends with one token drawn from the current p by inverse
+// CDF.  That guarantee needs drafts drawn from q; a tree filled by top-k
+// (deterministic drafts) does not give samples from q, so on such trees the
+// output is not exactly distributed as p.  The kernel still computes exactly
+// the rule above, which is what its parity with the reference walk checks.
 //
 // Greedy: one workgroup per (node, sequence) takes the target's argmax of
 // that node (first maximum), then the last workgroup of the sequence walks

@@ -33,16 +33,3 @@ def commit(k, v, ctx_len, accept_len, out_nodes, out_tokens):
         root_next[b] = int(out_tokens[b][n])
     return k2, v2, ctx_next, root_next
 
-
-def greedy_decode(prompt, n_tokens, logits_of):
-    """Plain greedy decoding: n_tokens times, append the first maximum of
-    logits_of(prefix).  The reference that multi-step greedy Medusa must
-    reproduce (P3, section 5: greedy speculative output equals greedy
-    decoding of the target)."""
-    seq = list(prompt)
-    out = []
-    for _ in range(n_tokens):
-        t = int(np.argmax(logits_of(seq)))
-        seq.append(t)
-        out.append(t)
-    return out

@@ -3,19 +3,18 @@
 Follows P1 ("Medusa 심층 아키텍처"), section "트리 어텐션 ... 고정 트리 토폴로지와
 2차원 어텐션 마스크": head d contributes its top candidates at depth d, a fixed
 topology combines them into paths, and the tree mask lets token i see token j
-iff j is an ancestor of i or j = i (0, else -inf).  P1's sketch code
-(``build_tree_attention_mask``) builds the same mask a second way: set the
-diagonal, then for each (child, parent) pair mark the parent and copy the
-parent's visible set into the child's row.
+iff j is an ancestor of i or j = i (0, else -inf).  The visible sets are built
+two independent ways here: by walking parent pointers, and as the reflexive
+transitive closure of the one-hop "parent of" relation (the least fixpoint of
+repeated boolean matrix products).
 
 Node numbering: node 0 is the root (the base model's token t+1); a node at
 depth d >= 1 carries candidate number rank(n) of Medusa head d (head index
 d-1), which predicts token t+d+1 (P1 section "Medusa의 핵심 철학", head list;
 P4 section 2.2).  Position of node n = ctx + depth(n).
 
-Reading: P1's sketch lost its indentation; the propagation is read as being
-inside the pair loop, which is correct when pairs arrive in topological order
-(parent before child).  We require parent[n] < n.
+Reading: P1's sketch of the mask builder lost its indentation; it is read as
+requiring parents before children, so every topology here has parent[n] < n.
 """
 from __future__ import annotations
 
@@ -73,23 +72,29 @@ def visible_bruteforce(parent: Sequence[int]) -> np.ndarray:
     return vis
 
 
-def mask_by_propagation(pairs, total_tokens: int) -> np.ndarray:
-    """The additive mask [T, T] (0 visible, -inf hidden) built the way P1's
-    sketch code describes: diagonal first, then per (child, parent) pair in
-    topological order, mark the parent and inherit the parent's row."""
-    mask = np.full((total_tokens, total_tokens), -np.inf)
-    for i in range(total_tokens):
-        mask[i, i] = 0.0
-    for child, par in pairs:
-        mask[child, par] = 0.0
-        for k in range(total_tokens):
-            if mask[par, k] == 0.0:
-                mask[child, k] = 0.0
-    return mask
+def visible_by_closure(parent: Sequence[int]) -> np.ndarray:
+    """Boolean [T, T] visibility as the reflexive transitive closure of the
+    one-hop relation up[i, parent(i)]: start from the identity and add one
+    more hop (a boolean matrix product) until no new pair appears.  A tree has
+    no cycles, so the loop ends after at most depth + 1 products."""
+    T = len(parent)
+    up = np.zeros((T, T), dtype=np.int64)
+    for n in range(T):
+        if int(parent[n]) >= 0:
+            up[n, int(parent[n])] = 1
+    vis = np.eye(T, dtype=bool)
+    reach = np.eye(T, dtype=np.int64)
+    while True:
+        reach = (reach @ up > 0).astype(np.int64)   # exactly one hop further
+        if not reach.any():
+            return vis
+        vis |= reach > 0
 
 
-def pairs_of(parent: Sequence[int]):
-    return [(n, int(parent[n])) for n in range(1, len(parent))]
+def additive_mask(vis: np.ndarray) -> np.ndarray:
+    """The [T, T] additive form of a visibility matrix: 0 where visible,
+    -inf where hidden (P1 tree-attention section)."""
+    return np.where(vis, 0.0, -np.inf)
 
 
 def bitmask_rows(vis: np.ndarray) -> np.ndarray:

@@ -52,10 +52,24 @@ def _check(hidden, w1, wlm, t, topk, tol, round_r, full_oracle=True, sample_rows
         ref_logits = oheads.medusa_heads(to64(hidden), to64(w1), to64(wlm), round_r=round_r)
         err = row_rel_err(g_logits.reshape(-1, V), ref_logits.reshape(-1, V))
         assert err <= tol, err
-        # and, away from near ties, the same indices as the oracle's own ranking
+        # the oracle's own ranking where it is decided: the kernel ranks its
+        # logits exactly (checked above) and they are within e_row of the
+        # fp64 ones, so a position whose fp64 value is more than 2 e_row from
+        # both neighbours in the ranking must hold the same index
         o_idx, _ = odense.dense_candidates(to64(hidden), to64(w1), to64(wlm), topk, round_r=round_r)
-        agree = (o_idx == g_idx).mean()
-        assert agree > 0.97, agree
+        e_row = np.max(np.abs(g_logits - ref_logits), axis=-1)
+        checked = 0
+        for m in range(M):
+            for d in range(K):
+                kd = topk[d]
+                srt = np.sort(ref_logits[m, d])[::-1][:kd + 1]
+                for j in range(kd):
+                    lo = np.inf if j == 0 else srt[j - 1] - srt[j]
+                    if min(lo, srt[j] - srt[j + 1]) > 2 * e_row[m, d]:
+                        assert g_idx[m, d, j] == o_idx[m, d, j], (m, d, j)
+                        checked += 1
+        print(f"[dense ranking] {checked} of {M * sum(topk)} ranked positions decided in fp64",
+              flush=True)
     else:
         # sampled (row, head) pairs: the oracle's residual block, then its
         # vocab product r @ W^T taken over chunks of the vocabulary

@@ -213,7 +213,7 @@ def test_multi_draft_siblings_are_lossless(n_children):
     rank[0] = 0
     rank[1:] = np.arange(n_children)
     base = np.stack([np.log(p)] + [np.zeros(V)] * n_children)
-    n = 30000
+    n = 100000
     counts = np.zeros(V)
     for i in range(n):
         toks = np.concatenate([[0], rng.choice(V, size=n_children, p=q)])
@@ -236,7 +236,7 @@ def test_two_level_chain_joint_distribution_is_target():
     q2 = rng.dirichlet(np.ones(V))
     parent, rank = synth.chain_tree(2)
     head = np.log(np.stack([q1, q2]))
-    n = 40000
+    n = 100000
     counts = np.zeros((V, V))
     for i in range(n):
         x1 = _sample_from(q1, rng)

@@ -63,9 +63,12 @@ def test_mask_two_constructions_agree(idx):
     parent, rank = list(_trees())[idx]
     T = len(parent)
     vis = tree.visible_bruteforce(parent)
-    prop = tree.mask_by_propagation(tree.pairs_of(parent), T)
-    np.testing.assert_array_equal(prop == 0.0, vis)
-    np.testing.assert_array_equal(np.isneginf(prop), ~vis)
+    clo = tree.visible_by_closure(parent)
+    np.testing.assert_array_equal(clo, vis)
+    mask = tree.additive_mask(clo)
+    assert mask.shape == (T, T)
+    np.testing.assert_array_equal(mask == 0.0, vis)
+    np.testing.assert_array_equal(np.isneginf(mask), ~vis)
 
 
 @pytest.mark.parametrize("idx", range(14))
