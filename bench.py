@@ -37,11 +37,16 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="vicuna7b-shaped")
+    p.add_argument("--workload", default="zephyr7b-shaped",
+                   help="default: the largest single-GPU workload (B=8, GQA, ctx 16384)")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-layers", type=int, default=32,
-                   help="attention layers the CPU oracle runs (scaled to all layers)")
+    p.add_argument("--cpu-layers", type=int, default=1,
+                   help="attention layers the CPU oracle runs (scaled to all L layers)")
+    p.add_argument("--cpu-seqs", type=int, default=1,
+                   help="sequences of those layers the CPU oracle runs (scaled to all B)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="CPU work to time (whole sampled steps, repeated)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="run only a plain device copy of MIB MiB (4 times) and exit: the "
                         "calibration run for HBM byte counters")
@@ -242,20 +247,30 @@ def _capture(fn):
     return g
 
 
-def _time_replays(run, reps, warmup):
-    """Mean ms per call of run() between two events on the launch stream."""
+def _time_each(run, reps, warmup):
+    """ms of every one of reps calls of run(), from events recorded on the
+    launch stream between consecutive calls (no synchronisation inside), and
+    their mean (first to last event / reps)."""
     import torch
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
         run()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    each = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    return each, ev[0].elapsed_time(ev[reps]) / reps
+
+
+def _pct(xs, scale=1.0, nd=2):
+    """p10 / median / p90 of xs (times scale)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64) * scale
+    return {"p10": round(float(np.percentile(a, 10)), nd), "p50": round(float(np.median(a)), nd),
+            "p90": round(float(np.percentile(a, 90)), nd)}
 
 
 def time_gpu(w, args):
@@ -273,16 +288,18 @@ def time_gpu(w, args):
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # exactly args.steps steps between two synchronisations; an event after
+    # every step gives the per-step distribution without any sync inside
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_wall = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         run()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step = ev[0].elapsed_time(ev[args.steps]) / args.steps
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
 
     # per-stage figures: each stage captured as its own graph and replayed
     # between events on the launch stream (no host time inside)
@@ -296,15 +313,37 @@ def time_gpu(w, args):
               "attention_batched": _capture(stage_attention_batched),
               "heads_dense": _capture(stage_heads_dense)}
     reps = max(5, args.steps)
-    stages_us = {n: 1000.0 * _time_replays(g.replay, reps, 3) for n, g in graphs.items()}
+    stages_us, stages_pct = {}, {}
+    for n, g in graphs.items():
+        each, mean_ms = _time_each(g.replay, reps, 3)
+        stages_us[n] = 1000.0 * mean_ms
+        stages_pct[n] = _pct(each, 1000.0)
     attn_call_us = stages_us["attention"] / w.L
-    return ms_per_step, wall_s, stages_us, attn_call_us
+    return ms_per_step, wall_s, stages_us, attn_call_us, _pct(step_ms, 1.0, 4), stages_pct
 
 
-def cpu_baseline(w, n_layers, min_seconds=10.0, max_steps=40):
-    """The oracle as it stands (NumPy, fp64) on the host cores: whole steps of
-    the same workload (attention on n_layers of the L layers, scaled to all
-    L), repeated until about min_seconds of CPU work have been timed."""
+def host_cpu() -> dict:
+    """The host's CPU model (from /proc/cpuinfo) and logical core count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "os_cpu_count": os.cpu_count()}
+
+
+def cpu_baseline(w, n_layers, n_seqs, min_seconds=10.0, max_steps=40):
+    """The oracle as it stands (NumPy, fp64: the precision its parity role
+    fixes; it is not tuned for speed) on the host cores, on a bounded sample
+    of one step of the same workload: heads, top-k/tree and acceptance in
+    full, tree attention on n_layers layers of n_seqs sequences scaled by
+    (L / n_layers) * (B / n_seqs) -- every layer and sequence has the same
+    shape and they are independent.  Sampled steps are repeated until about
+    min_seconds of CPU work have been timed."""
     import numpy as np
     import torch
     from medusa_tree_verification_amd import synth
@@ -319,7 +358,8 @@ def cpu_baseline(w, n_layers, min_seconds=10.0, max_steps=40):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    n_layers = min(n_layers, w.L)
+    n_layers = max(1, min(n_layers, w.L))
+    n_seqs = max(1, min(n_seqs, w.B))
     parent, rank = synth.cost_ordered_tree(w.topk, w.T)
     f64 = lambda t: t.to(torch.float64).numpy()
     hidden, w1, wlm = synth.head_inputs(w, "cpu")
@@ -328,14 +368,17 @@ def cpu_baseline(w, n_layers, min_seconds=10.0, max_steps=40):
     layers = []
     for l in range(n_layers):
         q, k, v, ctx = synth.attention_inputs(w, l, "cpu")
-        layers.append((f64(q), f64(k), f64(v), ctx.numpy()))
+        layers.append((f64(q[:n_seqs]), f64(k[:n_seqs]), f64(v[:n_seqs]), ctx.numpy()[:n_seqs]))
+        del q, k, v
     base = synth.normal((w.B, w.T, w.V), w.base_logit_std, synth.seed_for(w.cfg_id, synth.T_BASE)).numpy()
     ua = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_UACC)).numpy()
     us = synth.uniform((w.B, w.T), synth.seed_for(w.cfg_id, synth.T_USMP)).numpy()
     roots = synth.roots(w, "cpu").numpy()
+    scale_attn = (w.L / n_layers) * (w.B / n_seqs)
     tot = {"heads": 0.0, "candidates": 0.0, "attention": 0.0, "accept": 0.0}
+    timed = 0.0
     steps = 0
-    while steps < max_steps and (steps == 0 or sum(tot.values()) < min_seconds):
+    while steps < max_steps and (steps == 0 or timed < min_seconds):
         t0 = time.perf_counter()
         logits = oheads.medusa_heads(h64, w1_64, wlm64, round_r=w.dtype == "bf16")
         t1 = time.perf_counter()
@@ -351,8 +394,9 @@ def cpu_baseline(w, n_layers, min_seconds=10.0, max_steps=40):
         t4 = time.perf_counter()
         tot["heads"] += t1 - t0
         tot["candidates"] += t2 - t1
-        tot["attention"] += (t3 - t2) * w.L / n_layers
+        tot["attention"] += (t3 - t2) * scale_attn
         tot["accept"] += t4 - t3
+        timed += t4 - t0
         steps += 1
     per_step = sum(tot.values()) / steps
     return {
@@ -360,10 +404,12 @@ def cpu_baseline(w, n_layers, min_seconds=10.0, max_steps=40):
         "unit": "verify steps/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"{steps} {w.name} step(s): heads, top-k/tree and acceptance in full, tree "
-                   f"attention on {n_layers} of {w.L} layers scaled x{w.L / n_layers:g} "
-                   f"(fp64 NumPy); {sum(tot.values()):.1f} s of CPU work timed"),
+        "sample": (f"{steps} sampled {w.name} step(s) in fp64 NumPy: heads, top-k/tree and "
+                   f"acceptance in full; tree attention on {n_layers} of {w.L} layers x "
+                   f"{n_seqs} of {w.B} sequences, scaled x{scale_attn:g} (layers and sequences "
+                   f"are identical in shape and independent); {timed:.1f} s of CPU work timed"),
         "stage_s": {k: round(v / steps, 3) for k, v in tot.items()},
+        "host": host_cpu(),
     }
 
 
@@ -381,7 +427,7 @@ def main():
     if w.dtype != "bf16":
         sys.exit("bench.py times the bf16 workloads")
 
-    ms, wall_s, stages_us, attn_us = time_gpu(w, args)
+    ms, wall_s, stages_us, attn_us, step_pct, stages_pct = time_gpu(w, args)
     a_bytes = attention_bytes(w)
     h_bytes = heads_bytes(w)
     attn_gbs = a_bytes / (attn_us * 1e-6) / 1e9
@@ -441,6 +487,8 @@ def main():
             "hbm_frac": round(w.K * (w.H * w.H + w.H * w.V) * 2 / (stages_us["heads_dense"] * 1e-6) / 1e9
                               / HBM_PEAK_GBS, 4)},
         "stages_us": {k: round(v, 2) for k, v in stages_us.items()},
+        "step_ms_pct": step_pct,
+        "stages_us_pct": stages_pct,
         "wall_s_timed": round(wall_s, 4),
     }
     probe = read_probe()
@@ -450,7 +498,7 @@ def main():
     result["hbm_read_probe"] = probe
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_layers)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_layers, args.cpu_seqs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
