@@ -617,6 +617,349 @@ __global__ __launch_bounds__(64) void merge_splits(AttnArgs a) {
   *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv));
 }
 
+// ---- grouped-query shapes: every query row of a K/V head in one workgroup ----
+// For more than 128 query rows per K/V head (T * G, e.g. 64 nodes x 4 query
+// heads) the rows no longer fit the two-role kernel above without a second
+// workgroup staging the same K/V.  Here one workgroup of 8 waves takes all of
+// them (up to 256): wave w owns query tiles 2w and 2w + 1 (32 rows, Q in
+// registers) and every key of the split, so each K/V byte is staged into LDS
+// once and read from LDS once per wave.  There are no staging waves: every
+// wave writes its share of a 64-key block (8 K rows and 8 V rows) straight
+// from HBM into LDS with buffer loads (`buffer_load_dwordx4 ... lds`: lane i
+// of a load lands at the load's LDS base + 16 i, so each lane fetches the
+// chunk that belongs at its place under the swizzle), two blocks ahead, into
+// a ring of four slot arrays.  Each slot is a separate LDS object, so the
+// compiler's wait before a read covers only the loads into that slot.  Both
+// K and V stay key-major (rows of 256 bytes); P.V reads V through gfx950's
+// transposing LDS read (ds_read_b64_tr_b16: within 16 lanes, lanes 4r..4r+3
+// supply row r and lane i receives element i of the four rows), two reads
+// per MFMA giving a lane the 8 keys of one d that its P^T operand holds.
+// Swizzles (16-byte chunk c of row r at position c ^ f(r)): K f(r) = r & 15
+// (the conflict-free K layout of the kernel above); V f(r) = 2 * ((r & 3) |
+// 4 * (bit 2 of r ^ bit 3 of r)), under which the 32 lanes of either half of
+// a transposing read cover the 64 banks once (also for halves made of lane
+// groups {0, 2} and {1, 3}), checked on the host over every read.
+// One barrier per block; a block is taken as two 32-key halves (scores,
+// softmax, P.V each).  Waves 4-7 (which share SIMDs with waves 0-3) run half
+// a block behind on P.V, so a SIMD's softmax work overlaps the other wave's
+// MFMAs.  Block i - 1 stays in its slot through interval i: four slots,
+// loads two blocks ahead.
+// The loads' buffer resources end at the split's end, so keys past the
+// sequence read as zeros (never NaN into P.V) and are masked in the scores.
+constexpr int GQ_WAVES = 8;
+constexpr int GQ_TILES = 2;                      // query tiles per wave
+constexpr int GQ_ROWS = GQ_WAVES * GQ_TILES * 16;  // 256 query rows per workgroup
+constexpr int GQ_SLOT = 2 * KB * GROWB;          // one block: K rows, then V rows
+constexpr int GQ_AHEAD = 2;                      // blocks loaded ahead of use
+constexpr int GQ_MASK_WORDS = 1024;              // T * W <= 1024 (T <= 256)
+
+__device__ __forceinline__ int gq_vswz(int r) {
+  return 2 * ((r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void* gq_lds_ptr;
+
+__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+__global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char s0[GQ_SLOT], s1[GQ_SLOT], s2[GQ_SLOT], s3[GQ_SLOT];
+  __shared__ uint64_t smask[GQ_MASK_WORDS];
+  const int id = blockIdx.x;
+  const int task = (id & 7) * a.per_xcd + (id >> 3);
+  if (task >= a.tasks) return;  // whole workgroup leaves before any barrier
+  const int split = task % a.NS;
+  const int rest = task / a.NS;  // = lbh * QC + qc
+  const int qc = rest % a.QC;
+  const int lbh = rest / a.QC;   // = layer * B * Hkv + bh
+  const int bh = lbh % (a.B * a.Hkv);
+  const int layer = lbh / (a.B * a.Hkv);
+  const int b = bh / a.Hkv;
+  const int kvh = bh % a.Hkv;
+  const uint16_t* qL = a.q + layer * a.q_lstride;
+  uint16_t* outL = a.out + layer * a.out_lstride;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool late = wave >= 4;  // one stage behind on P.V
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+
+  int ctx = a.ctx[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.S_cap - a.T ? a.S_cap - a.T : ctx);
+  const int S = ctx + a.T;
+  const int k_begin = split * a.chunk;
+  const int k_end = (split == a.NS - 1) ? S : min(S, k_begin + a.chunk);
+  const int nblk = k_end > k_begin ? (k_end - k_begin + KB - 1) / KB : 0;
+
+  // Q fragments (tile t, k-step s: d-chunk 4s + grp of row l16) and mask rows
+  const int row0 = qc * GQ_ROWS + wave * GQ_TILES * 16;
+  auto q_ptr = [&](int r, int ch) __attribute__((always_inline)) {
+    const int node = r / a.G, gq = r % a.G;
+    return qL + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + ch * 8;
+  };
+  bf16x8 qf[GQ_TILES][4];
+  int qnode[GQ_TILES];
+#pragma unroll
+  for (int t = 0; t < GQ_TILES; ++t) {
+    const int r = row0 + t * 16 + l16;
+    qnode[t] = r < a.QR ? r / a.G : 0;
+    const int rc = min(r, a.QR - 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[t][s] = as_bf16x8(ldg16(q_ptr(rc, 4 * s + grp)));
+  }
+  const int nmask = a.T * a.W;
+  uint64_t mv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) mv[u] = a.mask[min(tid + 512 * u, nmask - 1)];
+  // Q and mask loads first: the mask's wait below then leaves the K/V loads in flight
+  __builtin_amdgcn_sched_barrier(0);
+
+  // this wave's share of every block: K rows and V rows 8w .. 8w + 7, as two
+  // loads of 4 rows each; lane i fills row i / 16 of a load at position i % 16
+  const uint16_t* kbase = a.k + layer * a.kv_lstride + static_cast<int64_t>(bh) * a.S_cap * D;
+  const uint16_t* vbase_g = a.v + layer * a.kv_lstride + static_cast<int64_t>(bh) * a.S_cap * D;
+  int koff[2], voff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 8 * wave + 4 * q + (lane >> 4), p = lane & 15;
+    koff[q] = r * GROWB + 16 * (p ^ (r & 15));
+    voff[q] = r * GROWB + 16 * (p ^ gq_vswz(r));
+  }
+  auto gload = [&](char* slot, int blk) __attribute__((always_inline)) {
+    const int kb = k_begin + blk * KB;
+    const int nrec = (k_end - kb) * GROWB;
+    const int64_t eoff = static_cast<int64_t>(kb) * D;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kbase + eoff), 0, nrec > 0 ? nrec : 0, RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vbase_g + eoff), 0, nrec > 0 ? nrec : 0, RSRC_WORD3);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (gq_lds_ptr)(slot + (8 * wave + 4 * q) * GROWB), 16,
+                                               koff[q], 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (gq_lds_ptr)(slot + K_TILE + (8 * wave + 4 * q) * GROWB),
+                                               16, voff[q], 0, 0, 0);
+  };
+  gload(s0, 0);
+  gload(s1, 1);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (tid + 512 * u < nmask) smask[tid + 512 * u] = mv[u];
+  const uint32_t* smask32 = reinterpret_cast<const uint32_t*>(smask);
+
+  f32x4 o[GQ_TILES][8];
+  float m_run[GQ_TILES], mu[GQ_TILES], l_run[GQ_TILES];
+#pragma unroll
+  for (int t = 0; t < GQ_TILES; ++t) {
+    m_run[t] = -INFINITY;
+    mu[t] = 0.f;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // K row kt * 16 + l16, chunk 4s + grp sits at kx0 ^ 64 s in the row
+  const int kx0 = 16 * (grp ^ l16);
+  // transposing V reads: row 32h + 16 s2 + 4 grp + (l16 >> 2), the 8 bytes of
+  // d = 16 dt + 4 (l16 & 3); the row's swizzle depends on its low 4 bits only
+  const int vr = 4 * grp + (l16 >> 2);
+  const int vx0 = K_TILE + vr * GROWB + 16 * (((l16 >> 1) & 1) ^ gq_vswz(vr)) + 8 * (l16 & 1);
+
+  // Scores and probabilities of one 32-key half (keys kb0 + 32h ..), P^T
+  // packed for P.V in pb[t].  A rescale of the state here covers o, which
+  // must therefore already hold every earlier half's P.V: each half's P.V is
+  // accumulated before the next half's softmax (the online softmax is exact
+  // for any split of the keys, as long as no probabilities taken against an
+  // older reference are added after a rescale).
+  auto qk_softmax = [&](const char* blk, int kb0, int h, uint4 (&pb)[GQ_TILES]) __attribute__((always_inline)) {
+    f32x4 sc[GQ_TILES][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const char* kr = blk + ((2 * h + st) * 16 + l16) * GROWB;
+      bf16x8 kf[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + (kx0 ^ (64 * s))));
+#pragma unroll
+      for (int t = 0; t < GQ_TILES; ++t) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[t][s], acc, 0, 0, 0);
+        sc[t][st] = acc;
+      }
+    }
+    const int kh = kb0 + 32 * h;
+    if (kh + 32 > ctx || kh + 32 > k_end) {  // the tree region or the split's end
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = kh + st * 16 + 4 * grp + e;
+          const int jj = key - ctx;
+          const int jc = jj < 0 ? 0 : (jj >= a.T ? a.T - 1 : jj);
+#pragma unroll
+          for (int t = 0; t < GQ_TILES; ++t) {
+            const uint32_t wv = smask32[qnode[t] * 2 * a.W + (jc >> 5)];
+            const bool vis = key < k_end && (jj < 0 || ((wv >> (jc & 31)) & 1u));
+            if (!vis) sc[t][st][e] = -INFINITY;
+          }
+        }
+      }
+    }
+    // reference max with slack, as in the kernel above
+    float lm[GQ_TILES];
+    bool over = false;
+#pragma unroll
+    for (int t = 0; t < GQ_TILES; ++t) {
+      lm[t] = fmaxf(fmaxf(fmaxf(sc[t][0][0], sc[t][0][1]), fmaxf(sc[t][0][2], sc[t][0][3])),
+                    fmaxf(fmaxf(sc[t][1][0], sc[t][1][1]), fmaxf(sc[t][1][2], sc[t][1][3])));
+      over |= lm[t] * a.scale_log2 > m_run[t] + RESCALE_SLACK;
+    }
+    if (__builtin_amdgcn_ballot_w64(over)) {
+#pragma unroll
+      for (int t = 0; t < GQ_TILES; ++t) {
+        const float mnew = fmaxf(m_run[t], rows_max(lm[t]) * a.scale_log2);
+        const float mu_new = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - mu_new);
+        m_run[t] = mnew;
+        mu[t] = mu_new;
+        l_run[t] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < GQ_TILES; ++t) {
+      float p[2][4];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[st][e] = __builtin_amdgcn_exp2f(fmaf(sc[t][st][e], a.scale_log2, -mu[t]));
+      l_run[t] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+      pb[t] = make_uint4(pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
+                         pack_bf16(p[1][2], p[1][3]));
+    }
+  };
+  // O^T += V^T P^T over the half's 32 keys
+  auto pv = [&](const char* blk, int h, const uint4 (&pb)[GQ_TILES]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const char* vp = blk + (vx0 ^ (32 * dt)) + 32 * h * GROWB;
+      const uint2 lo = lds_read_tr(vp);
+      const uint2 hi = lds_read_tr(vp + 16 * GROWB);
+      const bf16x8 va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+      for (int t = 0; t < GQ_TILES; ++t)
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(pb[t]), o[t][dt], 0, 0, 0);
+    }
+  };
+
+  // One block per interval: wait for this wave's loads of the block (the
+  // next block's 4 loads may still fly), pass the barrier, load two blocks
+  // ahead into the slot nobody reads any more, then compute.  The early
+  // waves take each half's scores, softmax and P.V in turn; the late waves
+  // first finish the previous block's second half (its P.V), then this
+  // block's first half and the scores and softmax of its second half, whose
+  // P^T they carry into the next interval.  The two roles run separate
+  // loops, so the carried P^T does not occupy registers in the other loop.
+  auto interval = [&](char* ahead, int i) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    gload(ahead, i + GQ_AHEAD);  // past the split: an empty resource, zeros, never read
+  };
+  if (!late) {
+    auto step = [&](char* cur, char* ahead, int i) __attribute__((always_inline)) {
+      interval(ahead, i);
+      if (i < nblk) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint4 pb[GQ_TILES];
+          qk_softmax(cur, k_begin + i * KB, h, pb);
+          pv(cur, h, pb);
+        }
+      }
+    };
+    for (int i = 0; i < nblk; i += 4) {
+      step(s0, s2, i);
+      step(s1, s3, i + 1);
+      step(s2, s0, i + 2);
+      step(s3, s1, i + 3);
+    }
+  } else {
+    uint4 pb_prev[GQ_TILES];
+    bool have_prev = false;
+    auto step = [&](char* cur, char* prev, char* ahead, int i) __attribute__((always_inline)) {
+      interval(ahead, i);
+      if (have_prev) pv(prev, 1, pb_prev);
+      have_prev = i < nblk;
+      if (have_prev) {
+        uint4 pb[GQ_TILES];
+        qk_softmax(cur, k_begin + i * KB, 0, pb);
+        pv(cur, 0, pb);
+        qk_softmax(cur, k_begin + i * KB, 1, pb_prev);
+      }
+    };
+    for (int i = 0; i < nblk; i += 4) {
+      step(s0, s3, s2, i);
+      step(s1, s0, s3, i + 1);
+      step(s2, s1, s0, i + 2);
+      step(s3, s2, s1, i + 3);
+    }
+    // the last second half's P.V: its block sits in the slot of block nblk - 1
+    if (have_prev) {
+      switch ((nblk - 1) & 3) {
+        case 0: pv(s0, 1, pb_prev); break;
+        case 1: pv(s1, 1, pb_prev); break;
+        case 2: pv(s2, 1, pb_prev); break;
+        default: pv(s3, 1, pb_prev); break;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // every load (also those past the split) has landed
+  __syncthreads();
+
+#pragma unroll
+  for (int t = 0; t < GQ_TILES; ++t) l_run[t] = rows_sum(l_run[t]);
+
+  const int BH = a.B * a.Hkv;
+#pragma unroll
+  for (int t = 0; t < GQ_TILES; ++t) {
+    const int r = row0 + t * 16 + l16;
+    if (r >= a.QR) continue;
+    if (a.NS == 1) {
+      const float inv = 1.0f / l_run[t];
+      const int node = r / a.G, gq = r % a.G;
+      uint16_t* op = outL + ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 v = o[t][dt] * inv;
+        *reinterpret_cast<uint2*>(op + dt * 16 + 4 * grp) =
+            make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+      }
+    } else {
+      const int64_t prow = (static_cast<int64_t>(split) * a.L * BH + lbh) * a.QRpad + r;
+      uint16_t* po = a.part_o + prow * D;
+      const float inv = l_run[t] > 0.f ? 1.0f / l_run[t] : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 v = o[t][dt] * inv;
+        *reinterpret_cast<uint2*>(po + dt * 16 + 4 * grp) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+      }
+      if (grp == 0)
+        *reinterpret_cast<float2*>(a.part_ml + ((static_cast<int64_t>(lbh) * a.QRpad + r) * a.NS + split) * 2) =
+            make_float2(m_run[t], l_run[t]);
+    }
+  }
+}
+
 // ---- fp32 path: one wave per (b, node, query head), keys in sequence ----
 struct AttnF32Args {
   const float* q;
@@ -676,6 +1019,7 @@ __global__ __launch_bounds__(256) void tree_attn_f32(AttnF32Args a) {
 // ---- launch planning -------------------------------------------------------
 struct Plan {
   int G, QR, NQT, QTW, QC, QRpad, NS, chunk;
+  bool gqa;  // more than 128 query rows per K/V head: tree_attn_gqa
   size_t ws_bytes, off_ml;
   int lds_bytes, lds_mask, lds_q, lds_ring;
 };
@@ -736,19 +1080,39 @@ int occupancy(int qtw, int lds) {
   return n;
 }
 
+int occupancy_gqa() {
+  static int n = 0;
+  if (!n) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&tree_attn_gqa), 512,
+                                                     0) != hipSuccess || n < 1) {
+      (void)hipGetLastError();
+      n = 1;
+    }
+  }
+  return n;
+}
+
 Plan make_plan(int B, int Hq, int Hkv, int ctx_max, int T, int W) {
   Plan p{};
   p.G = Hq / Hkv;
   p.QR = T * p.G;
   p.NQT = (p.QR + 15) / 16;
-  // at most 2 query tiles per compute wave (more would spill registers)
-  p.QC = (p.NQT + 7) / 8;
-  p.QTW = (p.NQT + 4 * p.QC - 1) / (4 * p.QC);
   p.QRpad = p.NQT * 16;
-  p.lds_mask = 0;
-  p.lds_q = static_cast<int>(round_up(static_cast<size_t>(T) * W * 8, 16));
-  p.lds_ring = p.lds_q + (p.QTW == 1 ? 0 : 4 * p.QTW * 16 * KROWB);
-  p.lds_bytes = p.lds_ring + NSLOT * BLK_BYTES;
+  p.gqa = p.NQT > 8;
+  if (p.gqa) {
+    // 256 query rows per workgroup, 2 tiles per wave, static LDS
+    p.QC = (p.NQT + 15) / 16;
+    p.QTW = GQ_TILES;
+    p.lds_bytes = 0;
+  } else {
+    // at most 2 query tiles per compute wave (more would spill registers)
+    p.QC = (p.NQT + 7) / 8;
+    p.QTW = (p.NQT + 4 * p.QC - 1) / (4 * p.QC);
+    p.lds_mask = 0;
+    p.lds_q = static_cast<int>(round_up(static_cast<size_t>(T) * W * 8, 16));
+    p.lds_ring = p.lds_q + (p.QTW == 1 ? 0 : 4 * p.QTW * 16 * KROWB);
+    p.lds_bytes = p.lds_ring + NSLOT * BLK_BYTES;
+  }
   const int Smax = ctx_max + T;
   const int base = B * Hkv * p.QC;
   int ns = env_int("MEDUSA_ATTN_SPLITS", 0);
@@ -756,7 +1120,7 @@ Plan make_plan(int B, int Hq, int Hkv, int ctx_max, int T, int W) {
     // the most splits whose workgroups all run in one round of the
     // resident slots (a second, partly filled round costs more than longer
     // splits do, and fewer splits leave CUs idle); at least one block each
-    const int slots = cu_count() * occupancy(p.QTW, p.lds_bytes);
+    const int slots = cu_count() * (p.gqa ? occupancy_gqa() : occupancy(p.QTW, p.lds_bytes));
     const int max_ns = (Smax + KB - 1) / KB;
     ns = slots / (base > 0 ? base : 1);
     if (ns > max_ns) ns = max_ns;
@@ -900,9 +1264,14 @@ int attention_launch(const void* q, const void* k_cache, const void* v_cache, in
   a.lds_q = p.lds_q;
   a.lds_ring = p.lds_ring;
   const int grid = 8 * a.per_xcd;
-  switch (p.QTW) {
-    case 1: rc = launch_cfg<1>(a, grid, p.lds_bytes, stream); break;
-    default: rc = launch_cfg<2>(a, grid, p.lds_bytes, stream); break;
+  if (p.gqa) {
+    hipLaunchKernelGGL(tree_attn_gqa, dim3(grid), dim3(512), 0, stream, a);
+    rc = check_launch("tree attention (bf16, grouped queries)");
+  } else {
+    switch (p.QTW) {
+      case 1: rc = launch_cfg<1>(a, grid, p.lds_bytes, stream); break;
+      default: rc = launch_cfg<2>(a, grid, p.lds_bytes, stream); break;
+    }
   }
   if (rc || p.NS == 1) return rc;
   const int64_t rows = static_cast<int64_t>(L) * B * Hkv * p.QR;

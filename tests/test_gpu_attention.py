@@ -43,6 +43,10 @@ SMALL = [
     ("t96", 1, 3, 3, ((10, 10, 5, 5), 96), [257], 0),
     ("t256-gqa8", 1, 8, 1, ((16, 8, 4, 2), 256), [64], 5),
     ("g5-odd", 2, 10, 2, ((6, 4, 3), 37), [31, 33], 1),
+    # more than 128 query rows per K/V head (the one-workgroup-per-head kernel)
+    ("gqa2-t96", 2, 8, 4, ((10, 10, 5, 5), 96), [1000, 517], 3),
+    ("gqa4-ctx0", 2, 8, 2, ((10, 10, 5, 5, 5), 64), [0, 64], 2),
+    ("gqa8-t33", 1, 16, 2, ((4, 3, 2), 33), [130], 0),
 ]
 
 
@@ -69,17 +73,40 @@ def test_attention_bf16_small_full(label, B, Hq, Hkv, tr, ctx, extra):
     assert err <= TOL_BF16, err
 
 
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (16, 4)])
 @pytest.mark.parametrize("splits", [1, 2, 3, 7])
-def test_attention_split_counts_agree(splits, monkeypatch):
-    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=2, Hq=4, Hkv=4, ctx=700, cfg_id=230)
+def test_attention_split_counts_agree(splits, hq, hkv, monkeypatch):
+    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=2, Hq=hq, Hkv=hkv, ctx=700, cfg_id=230)
     parent, rank = synth.cost_ordered_tree(w.topk, w.T)
     t = api.Tree(parent, rank, w.topk)
     q, k, v, ctx = synth.attention_inputs(w, 0, DEV)
     monkeypatch.setenv("MEDUSA_ATTN_SPLITS", str(splits))
-    announce("attention splits", splits)
+    announce("attention splits", splits, "heads", hq, hkv)
     out = api.tree_attention(q, k, v, ctx, w.ctx, t)
     torch.cuda.synchronize()
     ref = _oracle_full(q, k, v, ctx.tolist(), parent)
+    assert row_rel_err(to64(out), ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("splits", [2, 4, 8])
+def test_attention_gqa_tree_only_splits(splits, monkeypatch):
+    """Splits that hold only tree keys, where a deep node sees one key in each
+    32-key half of a block: the reference max moves between the halves, so
+    the first half's P.V must be in the output before the second half's
+    softmax rescales it (a 121-node random tree, short ragged contexts,
+    3 query heads per K/V head)."""
+    topk = (2, 4, 6, 2)
+    parent, rank = synth.random_tree(121, topk, 77)
+    t = api.Tree(parent, rank, topk)
+    ctx = [91, 57, 40]
+    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=3, Hq=12, Hkv=4, T=121, K=4, topk=topk,
+                                                  ctx=max(ctx), cfg_id=238)
+    q, k, v, ctx_t = synth.attention_inputs(w, 0, DEV, S_cap=max(ctx) + 121 + 5, ctx_lens=ctx)
+    monkeypatch.setenv("MEDUSA_ATTN_SPLITS", str(splits))
+    announce("attention gqa tree-only splits", splits)
+    out = api.tree_attention(q, k, v, ctx_t, max(ctx), t)
+    torch.cuda.synchronize()
+    ref = _oracle_full(q, k, v, ctx, parent)
     assert row_rel_err(to64(out), ref) <= TOL_BF16
 
 

@@ -87,11 +87,12 @@ def test_layers_fp32_small_full():
     _check_layers_full(q, k, v, ctx, parent, out, TOL_F32)
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 4), (16, 4)])
 @pytest.mark.parametrize("splits", [1, 3, 11])
-def test_layers_equal_per_layer_calls(splits, monkeypatch):
+def test_layers_equal_per_layer_calls(splits, hq, hkv, monkeypatch):
     """At a fixed split count, one grid over L layers computes exactly what L
     single-layer calls compute (same arithmetic per query row)."""
-    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=2, Hq=8, Hkv=4, ctx=900, cfg_id=320)
+    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=2, Hq=hq, Hkv=hkv, ctx=900, cfg_id=320)
     parent, rank = synth.cost_ordered_tree(w.topk, w.T)
     t = api.Tree(parent, rank, w.topk)
     L = 3
@@ -105,7 +106,7 @@ def test_layers_equal_per_layer_calls(splits, monkeypatch):
         assert torch.equal(out[l], one), l
 
 
-@pytest.mark.parametrize("name", ["vicuna7b-shaped", "vicuna13b-shaped"])
+@pytest.mark.parametrize("name", ["vicuna7b-shaped", "vicuna13b-shaped", "zephyr7b-shaped"])
 def test_layers_full_size_sampled_rows(name):
     """Every layer of the workload in one call, in the planner's own split
     count; the oracle recomputes sampled (layer, b, node, head) rows."""
