@@ -639,11 +639,13 @@ __global__ __launch_bounds__(64) void merge_splits(AttnArgs a) {
 // 4 * (bit 2 of r ^ bit 3 of r)), under which the 32 lanes of either half of
 // a transposing read cover the 64 banks once (also for halves made of lane
 // groups {0, 2} and {1, 3}), checked on the host over every read.
-// One barrier per block; a block is taken as two 32-key halves (scores,
-// softmax, P.V each).  Waves 4-7 (which share SIMDs with waves 0-3) run half
-// a block behind on P.V, so a SIMD's softmax work overlaps the other wave's
-// MFMAs.  Block i - 1 stays in its slot through interval i: four slots,
-// loads two blocks ahead.
+// One barrier per block; a block is taken as two 32-key halves, pipelined
+// within each wave so that MFMAs and the softmax's vector work are
+// independent neighbours, interleaved one MFMA to three vector instructions
+// (see the loop).  Each query's running sum of probabilities comes from one
+// more MFMA per tile and half (a ones operand against P^T), which sums the
+// same bf16 values P.V uses and takes the additions off the vector unit.
+// Four slots, loads two blocks ahead.
 // The loads' buffer resources end at the split's end, so keys past the
 // sequence read as zeros (never NaN into P.V) and are masked in the scores.
 constexpr int GQ_WAVES = 8;
@@ -686,7 +688,6 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool late = wave >= 4;  // one stage behind on P.V
   const int l16 = lane & 15;
   const int grp = lane >> 4;
 
@@ -756,15 +757,19 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
   const uint32_t* smask32 = reinterpret_cast<const uint32_t*>(smask);
 
   f32x4 o[GQ_TILES][8];
-  float m_run[GQ_TILES], mu[GQ_TILES], l_run[GQ_TILES];
+  // lsum[t]: every element holds the running sum of the query's probabilities
+  // (as bf16, the values P.V uses), accumulated by an MFMA against ones
+  f32x4 lsum[GQ_TILES];
+  float m_run[GQ_TILES], mu[GQ_TILES];
 #pragma unroll
   for (int t = 0; t < GQ_TILES; ++t) {
     m_run[t] = -INFINITY;
     mu[t] = 0.f;
-    l_run[t] = 0.f;
+    lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const bf16x8 ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
   // K row kt * 16 + l16, chunk 4s + grp sits at kx0 ^ 64 s in the row
   const int kx0 = 16 * (grp ^ l16);
   // transposing V reads: row 32h + 16 s2 + 4 grp + (l16 >> 2), the 8 bytes of
@@ -772,14 +777,8 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
   const int vr = 4 * grp + (l16 >> 2);
   const int vx0 = K_TILE + vr * GROWB + 16 * (((l16 >> 1) & 1) ^ gq_vswz(vr)) + 8 * (l16 & 1);
 
-  // Scores and probabilities of one 32-key half (keys kb0 + 32h ..), P^T
-  // packed for P.V in pb[t].  A rescale of the state here covers o, which
-  // must therefore already hold every earlier half's P.V: each half's P.V is
-  // accumulated before the next half's softmax (the online softmax is exact
-  // for any split of the keys, as long as no probabilities taken against an
-  // older reference are added after a rescale).
-  auto qk_softmax = [&](const char* blk, int kb0, int h, uint4 (&pb)[GQ_TILES]) __attribute__((always_inline)) {
-    f32x4 sc[GQ_TILES][2];
+  // Scores of one 32-key half (keys kh .. kh + 31): the MFMAs, then the mask.
+  auto qk_mma = [&](const char* blk, int h, f32x4 (&sc)[GQ_TILES][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const char* kr = blk + ((2 * h + st) * 16 + l16) * GROWB;
@@ -794,7 +793,8 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
         sc[t][st] = acc;
       }
     }
-    const int kh = kb0 + 32 * h;
+  };
+  auto qk_mask = [&](int kh, f32x4 (&sc)[GQ_TILES][2]) __attribute__((always_inline)) {
     if (kh + 32 > ctx || kh + 32 > k_end) {  // the tree region or the split's end
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -812,13 +812,21 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
         }
       }
     }
-    // reference max with slack, as in the kernel above
+  };
+  // The softmax of a half in two parts.  pre(): the reference max with
+  // slack, as in the kernel above; when it moves, the state is rescaled --
+  // o, the running sum and, if a half's P^T is still waiting for its P.V
+  // (pending), that P^T too, so that it matches the new reference.
+  // expo(): the probabilities against the current reference, P^T packed for
+  // P.V in pb[t].
+  auto pre = [&](const f32x4 (&sc)[GQ_TILES][2], uint4* pending) __attribute__((always_inline)) {
     float lm[GQ_TILES];
     bool over = false;
 #pragma unroll
     for (int t = 0; t < GQ_TILES; ++t) {
-      lm[t] = fmaxf(fmaxf(fmaxf(sc[t][0][0], sc[t][0][1]), fmaxf(sc[t][0][2], sc[t][0][3])),
-                    fmaxf(fmaxf(sc[t][1][0], sc[t][1][1]), fmaxf(sc[t][1][2], sc[t][1][3])));
+      lm[t] = fmaxf(__builtin_fmaxf(__builtin_fmaxf(sc[t][0][0], sc[t][0][1]), sc[t][0][2]),
+                    __builtin_fmaxf(__builtin_fmaxf(sc[t][0][3], sc[t][1][0]), sc[t][1][1]));
+      lm[t] = fmaxf(lm[t], fmaxf(sc[t][1][2], sc[t][1][3]));
       over |= lm[t] * a.scale_log2 > m_run[t] + RESCALE_SLACK;
     }
     if (__builtin_amdgcn_ballot_w64(over)) {
@@ -829,11 +837,20 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
         const float alpha = __builtin_amdgcn_exp2f(m_run[t] - mu_new);
         m_run[t] = mnew;
         mu[t] = mu_new;
-        l_run[t] *= alpha;
+        lsum[t] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
+        if (pending) {
+          uint4& w = pending[t];
+          auto sc2 = [&](uint32_t x) {
+            return pack_bf16(bf16_bits_to_f32(x & 0xffffu) * alpha, bf16_bits_to_f32(x >> 16) * alpha);
+          };
+          w = make_uint4(sc2(w.x), sc2(w.y), sc2(w.z), sc2(w.w));
+        }
       }
     }
+  };
+  auto expo = [&](const f32x4 (&sc)[GQ_TILES][2], uint4 (&pb)[GQ_TILES]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < GQ_TILES; ++t) {
       float p[2][4];
@@ -841,13 +858,15 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[st][e] = __builtin_amdgcn_exp2f(fmaf(sc[t][st][e], a.scale_log2, -mu[t]));
-      l_run[t] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
       pb[t] = make_uint4(pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]), pack_bf16(p[1][0], p[1][1]),
                          pack_bf16(p[1][2], p[1][3]));
     }
   };
   // O^T += V^T P^T over the half's 32 keys
   auto pv = [&](const char* blk, int h, const uint4 (&pb)[GQ_TILES]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < GQ_TILES; ++t)
+      lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pb[t]), lsum[t], 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const char* vp = blk + (vx0 ^ (32 * dt)) + 32 * h * GROWB;
@@ -862,72 +881,57 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
 
   // One block per interval: wait for this wave's loads of the block (the
   // next block's 4 loads may still fly), pass the barrier, load two blocks
-  // ahead into the slot nobody reads any more, then compute.  The early
-  // waves take each half's scores, softmax and P.V in turn; the late waves
-  // first finish the previous block's second half (its P.V), then this
-  // block's first half and the scores and softmax of its second half, whose
-  // P^T they carry into the next interval.  The two roles run separate
-  // loops, so the carried P^T does not occupy registers in the other loop.
-  auto interval = [&](char* ahead, int i) __attribute__((always_inline)) {
+  // ahead into the slot nobody reads any more, then compute the block as a
+  // short software pipeline whose MFMA and VALU parts are independent: the
+  // second half's scores next to the first half's exponentials, the first
+  // half's P.V next to the second half's exponentials.  A rescale at the
+  // second half also rescales the first half's waiting P^T.
+  auto step = [&](char* cur, char* ahead, int i) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     gload(ahead, i + GQ_AHEAD);  // past the split: an empty resource, zeros, never read
-  };
-  if (!late) {
-    auto step = [&](char* cur, char* ahead, int i) __attribute__((always_inline)) {
-      interval(ahead, i);
-      if (i < nblk) {
+    if (i < nblk) {
+      const int kb0 = k_begin + i * KB;
+      f32x4 sc0[GQ_TILES][2], sc1[GQ_TILES][2];
+      uint4 pb0[GQ_TILES], pb1[GQ_TILES];
+      qk_mma(cur, 0, sc0);
+      qk_mask(kb0, sc0);
+      pre(sc0, nullptr);
+      // second half's scores (16 MFMAs) beside the first half's exponentials
+      qk_mma(cur, 1, sc1);
+      expo(sc0, pb0);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint4 pb[GQ_TILES];
-          qk_softmax(cur, k_begin + i * KB, h, pb);
-          pv(cur, h, pb);
-        }
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
-    };
-    for (int i = 0; i < nblk; i += 4) {
-      step(s0, s2, i);
-      step(s1, s3, i + 1);
-      step(s2, s0, i + 2);
-      step(s3, s1, i + 3);
-    }
-  } else {
-    uint4 pb_prev[GQ_TILES];
-    bool have_prev = false;
-    auto step = [&](char* cur, char* prev, char* ahead, int i) __attribute__((always_inline)) {
-      interval(ahead, i);
-      if (have_prev) pv(prev, 1, pb_prev);
-      have_prev = i < nblk;
-      if (have_prev) {
-        uint4 pb[GQ_TILES];
-        qk_softmax(cur, k_begin + i * KB, 0, pb);
-        pv(cur, 0, pb);
-        qk_softmax(cur, k_begin + i * KB, 1, pb_prev);
+      qk_mask(kb0 + 32, sc1);
+      pre(sc1, pb0);
+      // first half's P.V (18 MFMAs) beside the second half's exponentials
+      pv(cur, 0, pb0);
+      expo(sc1, pb1);
+#pragma unroll
+      for (int g = 0; g < 18; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
       }
-    };
-    for (int i = 0; i < nblk; i += 4) {
-      step(s0, s3, s2, i);
-      step(s1, s0, s3, i + 1);
-      step(s2, s1, s0, i + 2);
-      step(s3, s2, s1, i + 3);
+      pv(cur, 1, pb1);
     }
-    // the last second half's P.V: its block sits in the slot of block nblk - 1
-    if (have_prev) {
-      switch ((nblk - 1) & 3) {
-        case 0: pv(s0, 1, pb_prev); break;
-        case 1: pv(s1, 1, pb_prev); break;
-        case 2: pv(s2, 1, pb_prev); break;
-        default: pv(s3, 1, pb_prev); break;
-      }
-    }
+  };
+  for (int i = 0; i < nblk; i += 4) {
+    step(s0, s2, i);
+    step(s1, s3, i + 1);
+    step(s2, s0, i + 2);
+    step(s3, s1, i + 3);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // every load (also those past the split) has landed
   __syncthreads();
 
+  float l_run[GQ_TILES];
 #pragma unroll
-  for (int t = 0; t < GQ_TILES; ++t) l_run[t] = rows_sum(l_run[t]);
+  for (int t = 0; t < GQ_TILES; ++t) l_run[t] = lsum[t][0];
 
   const int BH = a.B * a.Hkv;
 #pragma unroll
