@@ -285,6 +285,30 @@ int medusa_tree_attention_layers(const void* q, const void* k_cache, const void*
                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * medusa_tree_attention without allocation or workspace
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, layouts and results as medusa_tree_attention (the same kernels
+ * and launch plan), minus the workspace: the split partials live in a fixed
+ * device array of the library, MEDUSA_ATTENTION_SCRATCH_BYTES (32 MiB) per
+ * GPU, held until the process ends.  A call whose partials would exceed it
+ * (medusa_tree_attention_workspace_size above the limit) returns
+ * MEDUSA_EWORKSPACE before anything is enqueued.  The call never calls
+ * hipMalloc or hipFree; its first call on a device looks up that device's
+ * copy of the array (hipGetSymbolAddress).  Every call on one GPU shares that
+ * GPU's array and it keeps the last call's contents (nothing in it needs
+ * clearing): calls that overlap on one GPU, e.g. on two streams, race and must
+ * be serialised by the caller.
+ * ------------------------------------------------------------------------ */
+#define MEDUSA_ATTENTION_SCRATCH_BYTES (32u << 20)
+
+int medusa_tree_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* ctx_len, int ctx_max, const medusa_tree_t* tree,
+                                  int B, int Hq, int Hkv, int D, int S_cap, float scale,
+                                  medusa_dtype_t dt, void* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Stage 6: path acceptance
  *
  * temperature == 0: greedy.  P3, section 5 (greedy check) and P4, section

@@ -47,6 +47,9 @@ SIGNATURES = {
                                              c_int, P_void, c_int, c_void_p, c_int, c_int, c_int,
                                              c_int, c_int, c_float, c_int, P_void, P_void,
                                              c_size_t, P_void]),
+    "medusa_tree_attention_noalloc": (c_int, [P_void, P_void, P_void, P_void, c_int, c_void_p,
+                                              c_int, c_int, c_int, c_int, c_int, c_float, c_int,
+                                              P_void, P_void]),
     "medusa_accept_workspace_size": (c_size_t, [c_int, c_int, c_void_p, c_float]),
     "medusa_accept_paths": (c_int, [P_void, P_void, P_void, c_void_p, P_void, P_void, c_float,
                                     c_int, c_int, P_void, P_void, P_void, P_void, c_size_t,

@@ -283,6 +283,37 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     return out
 
 
+ATTENTION_SCRATCH_BYTES = 32 << 20
+
+
+def tree_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           ctx_len: torch.Tensor, ctx_max: int, tree: Tree,
+                           scale: Optional[float] = None, out=None, stream=None) -> torch.Tensor:
+    """medusa_tree_attention_noalloc: tree_attention with the split partials in
+    the library's fixed per-device scratch (no workspace, no allocation in the
+    call).  ``out`` must be given by callers that cannot allocate."""
+    lib = _lib.load()
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("need q [B,T,Hq,D] and k_cache/v_cache [B,Hkv,S_cap,D]")
+    B, T, Hq, D = q.shape
+    Hkv, S_cap = k_cache.shape[1], k_cache.shape[2]
+    _expect(q, "q", (B, tree.T, Hq, D), _FLOAT)
+    _expect(k_cache, "k_cache", (B, Hkv, S_cap, D), q.dtype)
+    _expect(v_cache, "v_cache", (B, Hkv, S_cap, D), q.dtype)
+    _expect(ctx_len, "ctx_len", (B,), torch.int32)
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, "out", tuple(q.shape), q.dtype)
+    _check(lib.medusa_tree_attention_noalloc(_ptr(q, "q"), _ptr(k_cache, "k_cache"),
+                                             _ptr(v_cache, "v_cache"), _ptr(ctx_len, "ctx_len"),
+                                             ctx_max, tree.handle, B, Hq, Hkv, D, S_cap,
+                                             float(scale), dt, _ptr(out, "out"), _stream(stream)))
+    return out
+
+
 def tree_attention_layers_workspace_size(L, B, Hq, Hkv, D, ctx_max, tree: Tree, dtype) -> int:
     return _lib.load().medusa_tree_attention_layers_workspace_size(
         L, B, Hq, Hkv, D, ctx_max, tree.handle, F32 if dtype == torch.float32 else BF16)

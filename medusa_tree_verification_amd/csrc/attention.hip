@@ -50,6 +50,7 @@
 //   i % 8), which keeps their partials in one L2.
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -1334,4 +1335,72 @@ extern "C" int medusa_tree_attention_layers(const void* q, const void* k_cache, 
   return attention_launch(q, k_cache, v_cache, q_layer_stride, kv_layer_stride, out_layer_stride, L,
                           ctx_len, ctx_max, tree, B, Hq, Hkv, D_, S_cap, scale, dt, out, ws,
                           ws_bytes, stream);
+}
+
+// ---- the no-allocation variant of medusa_tree_attention ---------------------
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid allocation): the split
+// partials live in a fixed array of this library's module instead of a
+// caller's workspace.  Each GPU the library runs on holds its own copy until
+// the process ends; the host-side name is only a stand-in, so its device
+// address is taken once per device with hipGetSymbolAddress (with that device
+// current) and that address is what the kernels receive.  Every call on a
+// GPU shares that GPU's array: calls that overlap on one GPU (e.g. on two
+// streams) race.  Nothing in it needs clearing: every partial a merge reads
+// is written by the same call first.
+static __device__ __align__(256) char scratch[MEDUSA_ATTENTION_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex scratch_mutex;
+void* scratch_ptr[64] = {nullptr};
+
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  const hipError_t e0 = hipGetDevice(&dev);
+  if (e0 != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    set_error("no usable current device for the attention scratch (device %d)", dev);
+    return MEDUSA_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      set_error("hipGetSymbolAddress of the attention scratch failed on device %d: %s", dev,
+                hipGetErrorString(e));
+      return MEDUSA_EHIP;
+    }
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
+extern "C" int medusa_tree_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                             const int32_t* ctx_len, int ctx_max,
+                                             const medusa_tree_t* tree, int B, int Hq, int Hkv,
+                                             int D_, int S_cap, float scale, medusa_dtype_t dt,
+                                             void* out, hipStream_t stream) {
+  clear_error();
+  // host-only sizing first: invalid arguments give 0 here and are reported
+  // by the launch below
+  const size_t need = medusa_tree_attention_workspace_size(B, Hq, Hkv, D_, ctx_max, tree, dt);
+  if (need > MEDUSA_ATTENTION_SCRATCH_BYTES) {
+    set_error("tree attention needs %zu bytes of split partials; the no-allocation call's scratch "
+              "holds %zu (use medusa_tree_attention with a workspace)",
+              need, static_cast<size_t>(MEDUSA_ATTENTION_SCRATCH_BYTES));
+    return MEDUSA_EWORKSPACE;
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = scratch_for_current_device(&ws);
+    if (rc) return rc;
+  }
+  return attention_launch(q, k_cache, v_cache, 0, 0, 0, 1, ctx_len, ctx_max, tree, B, Hq, Hkv, D_,
+                          S_cap, scale, dt, out, ws, ws ? MEDUSA_ATTENTION_SCRATCH_BYTES : 0, stream);
 }
