@@ -247,22 +247,32 @@ def _capture(fn):
     return g
 
 
-def _time_each(run, reps, warmup):
-    """ms of every one of reps calls of run(), from events recorded on the
-    launch stream between consecutive calls (no synchronisation inside), and
-    their mean (first to last event / reps)."""
+def _time_mean(run, reps):
+    """Mean ms per call of reps back-to-back calls of run(), between two
+    events on the launch stream (nothing else inside the timed region)."""
     import torch
-    for _ in range(warmup):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
         run()
+    e1.record()
     torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _time_each(run, reps):
+    """ms of each of reps calls of run(), from an event recorded after every
+    call (a separate pass: the events themselves add a little time between
+    calls, so means come from _time_mean)."""
+    import torch
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     ev[0].record()
     for i in range(reps):
         run()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    each = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
-    return each, ev[0].elapsed_time(ev[reps]) / reps
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
 
 
 def _pct(xs, scale=1.0, nd=2):
@@ -288,18 +298,13 @@ def time_gpu(w, args):
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    # exactly args.steps steps between two synchronisations; an event after
-    # every step gives the per-step distribution without any sync inside
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # exactly args.steps steps between two synchronisations and two events
     t_wall = time.perf_counter()
-    ev[0].record()
-    for i in range(args.steps):
-        run()
-        ev[i + 1].record()
-    torch.cuda.synchronize()
+    ms_per_step = _time_mean(run, args.steps)
     wall_s = time.perf_counter() - t_wall
-    ms_per_step = ev[0].elapsed_time(ev[args.steps]) / args.steps
-    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    # the per-step distribution from a second pass of as many steps, with an
+    # event after every step (not part of the timed region above)
+    step_ms = _time_each(run, args.steps)
 
     # per-stage figures: each stage captured as its own graph and replayed
     # between events on the launch stream (no host time inside)
@@ -315,9 +320,11 @@ def time_gpu(w, args):
     reps = max(5, args.steps)
     stages_us, stages_pct = {}, {}
     for n, g in graphs.items():
-        each, mean_ms = _time_each(g.replay, reps, 3)
-        stages_us[n] = 1000.0 * mean_ms
-        stages_pct[n] = _pct(each, 1000.0)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        stages_us[n] = 1000.0 * _time_mean(g.replay, reps)
+        stages_pct[n] = _pct(_time_each(g.replay, reps), 1000.0)
     attn_call_us = stages_us["attention"] / w.L
     return ms_per_step, wall_s, stages_us, attn_call_us, _pct(step_ms, 1.0, 4), stages_pct
 
