@@ -200,3 +200,60 @@ def test_graph_replays_rejection_sampling(V):
         torch.cuda.synchronize()
         for a, b in zip(acc, ref):
             assert torch.equal(a, b), f"eager call after replay {rep} differs"
+
+
+def test_graph_replays_grouped_query_attention():
+    """The grouped-query kernel (256 query rows per K/V head) in a graph:
+    per-layer calls with split partials in one shared workspace, the
+    all-layers call and the no-allocation call (partials in the library's
+    scratch); four replays with eager work between, each equal to eager."""
+    w = synth.WORKLOADS["zephyr7b-shaped"].scaled(B=2, Hq=8, Hkv=2, L=2, ctx=3000, cfg_id=330)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    tree = api.Tree(parent, rank, w.topk)
+    ctx_lens = [3000, 2210]
+    layers = [synth.attention_inputs(w, l, DEV, ctx_lens=ctx_lens) for l in range(w.L)]
+    ctx = layers[0][3]
+    q_all = torch.stack([x[0] for x in layers])
+    k_all = torch.stack([x[1] for x in layers])
+    v_all = torch.stack([x[2] for x in layers])
+    ws = torch.zeros(max(256, api.tree_attention_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.ctx, tree,
+                                                               torch.bfloat16)), dtype=torch.uint8, device=DEV)
+    ws_l = torch.zeros(max(256, api.tree_attention_layers_workspace_size(w.L, w.B, w.Hq, w.Hkv, w.D, w.ctx, tree,
+                                                                        torch.bfloat16)), dtype=torch.uint8, device=DEV)
+    outs = [torch.empty_like(layers[0][0]) for _ in range(w.L)]
+    out_all = torch.empty_like(q_all)
+    out_na = torch.empty_like(layers[0][0])
+
+    def run():
+        for l, (q, k, v, _) in enumerate(layers):
+            api.tree_attention(q, k, v, ctx, w.ctx, tree, out=outs[l], ws=ws)
+        api.tree_attention_layers(q_all, k_all, v_all, ctx, w.ctx, tree, out=out_all, ws=ws_l)
+        q, k, v, _ = layers[1]
+        api.tree_attention_noalloc(q, k, v, ctx, w.ctx, tree, out=out_na)
+
+    announce("graph: grouped-query attention, eager reference")
+    run()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in [*outs, out_all, out_na]]
+    assert torch.equal(out_na, outs[1])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for x in [*outs, out_all, out_na]:
+            x.zero_()
+        # eager work between replays, on other inputs, through the same workspaces
+        q, k, v, _ = layers[0]
+        api.tree_attention(q, k, v, ctx, w.ctx, tree, out=torch.empty_like(q), ws=ws)
+        torch.cuda.synchronize()
+        announce("graph: grouped-query replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip([*outs, out_all, out_na], ref):
+            assert torch.equal(got, exp), rep
