@@ -36,6 +36,8 @@
 //   row's top-kmax (logit, column) pairs written as that tile's candidates.
 //   A second kernel merges every row's tile candidates into each head's
 //   top-k.  The fp32 logits reach HBM only when the caller asks for them.
+#include <cfloat>
+
 #include "internal.h"
 
 using namespace medusa;
@@ -288,11 +290,13 @@ __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
 // written straight into LDS by buffer loads (`buffer_load_dwordx4 ... lds`:
 // lane i of a wave's load lands at the wave's LDS base + 16 i, so each lane
 // fetches the chunk that belongs at its position) into a ring of four stage
-// buffers, three steps ahead.  Each step: wait for this wave's loads of the
-// step and its own LDS reads of the previous one, one barrier, issue the
-// loads three steps ahead into the buffer everybody finished reading, then
-// the MFMAs.  The four buffers are separate LDS objects so that the
-// compiler's wait for the loads into one does not cover the others.
+// buffers, four steps ahead of their MFMAs.  The MFMA operands go LDS ->
+// registers one step ahead (two register sets), so the MFMAs of a step run
+// on fragments already in registers while the next step's are read: with
+// two waves per SIMD meeting at every barrier, an LDS round trip between the
+// barrier and the first MFMA left the matrix cores idle for most of the
+// step.  The buffers are separate LDS objects so that the compiler's wait
+// for the loads into one does not cover the others.
 constexpr int B2M = 256, B2N = 256, B2K = 32;
 constexpr int B2ROW = B2K * 2;               // 64 bytes per staged row
 constexpr int B2X = B2M * B2ROW;             // X tile bytes; the W tile follows
@@ -356,37 +360,61 @@ __global__ __launch_bounds__(512) void dense_gemm_big(DenseArgs a) {
   const int cx = 16 * (g ^ b2swz(l16));
   const int xrow = (wm * 64 + l16) * B2ROW + cx;
   const int wrow = B2X + (wn * 128 + l16) * B2ROW + cx;
-  auto compute = [&](const char* st) __attribute__((always_inline)) {
-    bf16x8 xf[4], wf[8];
+  // operand fragments of one k-step: [0, 4) X rows, [4, 12) W rows
+  auto read = [&](bf16x8 (&f)[12], const char* st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(st + xrow + i * 16 * B2ROW));
+    for (int i = 0; i < 4; ++i) f[i] = as_bf16x8(*reinterpret_cast<const uint4*>(st + xrow + i * 16 * B2ROW));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wf[j] = as_bf16x8(*reinterpret_cast<const uint4*>(st + wrow + j * 16 * B2ROW));
+    for (int j = 0; j < 8; ++j) f[4 + j] = as_bf16x8(*reinterpret_cast<const uint4*>(st + wrow + j * 16 * B2ROW));
+  };
+  auto mma = [&](const bf16x8 (&f)[12]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[4 + j], f[i], acc[i][j], 0, 0, 0);
   };
-  // s_waitcnt vmcnt(8) lgkmcnt(0) (expcnt untouched): this wave's loads of
-  // the current step are in (the two later steps' 8 loads may still fly) and
-  // its reads of the previous step's buffer are done
-  auto step = [&](char* cur, char* nxt, int ks) __attribute__((always_inline)) {
+  // Step k multiplies the fragments read during step k - 1 while it reads
+  // step k + 1's, so the barrier is never followed by an LDS round trip
+  // before the first MFMA.  At its top a wave waits for its own loads of
+  // step k + 1 (s_waitcnt vmcnt(8) lgkmcnt(0): steps k + 2 and k + 3 may
+  // still fly) and for its reads of step k's buffer; after the barrier every
+  // wave's step k + 1 bytes are in LDS and nobody reads step k's buffer any
+  // more, so the loads of step k + 4 go there.
+  auto step = [&](const bf16x8 (&cur)[12], bf16x8 (&nxt)[12], const char* rd, char* buf, int ks)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x0078);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    dma(nxt, ks + 3);  // past the end: bytes of the next row or zeros, never read
-    compute(cur);
+    dma(buf, ks + 4);  // past the end: bytes of the next row or zeros, never used
+    read(nxt, rd);     // past the end (last step): in-bounds LDS, never used
+    mma(cur);
+    // one LDS read between pairs of MFMAs, the loads up front
+    __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+#pragma unroll
+    for (int r = 0; r < 12; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
   const int nk = a.Kd / B2K;  // a multiple of 4
+  bf16x8 f0[12], f1[12];
   dma(st0, 0);
   dma(st1, 1);
   dma(st2, 2);
+  dma(st3, 3);
+  __builtin_amdgcn_s_waitcnt(0x007c);  // vmcnt(12): this wave's loads of step 0 are in
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read(f0, st0);
   for (int ks = 0; ks < nk; ks += 4) {
-    step(st0, st3, ks);
-    step(st1, st0, ks + 1);
-    step(st2, st1, ks + 2);
-    step(st3, st2, ks + 3);
+    step(f0, f1, st1, st0, ks);
+    step(f1, f0, st2, st1, ks + 1);
+    step(f0, f1, st3, st2, ks + 2);
+    step(f1, f0, st0, st3, ks + 3);
   }
   // every load (also those past the end) has landed before LDS is reused
   __builtin_amdgcn_s_waitcnt(0x0070);
@@ -416,6 +444,215 @@ __global__ __launch_bounds__(512) void dense_gemm_big(DenseArgs a) {
       }
     }
   } else {
+    // ---- the tile's per-row top-kmax, from the accumulators ---------------
+    // Local row r = wm*64 + 16i + l16 is held by 8 lanes, slot sl = wn*4 + g
+    // (lanes l16 + 16g of waves (wm, 0) and (wm, 1)); each holds, in
+    // acc[i][j], columns wn*128 + 16j + 4g + e: 8 granules of 4 columns.
+    //  1. every lane: its 8 granule maxima and the 3 largest of them
+    //  2. a thread per row: T = the kmax-th largest of the row's 24 such
+    //     maxima.  They are maxima of 24 distinct granules, so at least kmax
+    //     values of the row reach T: every value of the row's top kmax does
+    //  3. every lane appends its granules whose maximum reaches T to its
+    //     row's list (an LDS counter per row)
+    //  4. a thread per row moves the values >= T of those granules to the
+    //     front of the same bytes and 5. ranks them into its list (larger
+    //     value first, equal values by lower column, whatever order the
+    //     granules arrived in).
+    // On normally distributed logits a row keeps about kmax + 1 values.  A
+    // row with more than FT_CAP granules reaching T (many equal logits)
+    // sends the whole tile to the general epilogue further down.
+    constexpr int FT_CAP = 24;                  // granules per row
+    constexpr int FT_META = FT_CAP * 1024;      // granule index bytes
+    constexpr int FT_COL = FT_META + FT_CAP * 64;  // column bytes of the kept values
+    constexpr int FT_TAIL = B2STAGE - 512;      // the rows' thresholds, then their counters
+    static_assert(FT_COL + FT_CAP * 256 <= FT_TAIL, "row lists exceed a stage buffer");
+    // rows 64b .. 64b + 63 live in stage buffer b, slot-major (lanes of
+    // consecutive rows touch consecutive 16-byte chunks): granule slot s of
+    // row r at s * 1024 + (r & 63) * 16, its index byte at
+    // FT_META + s * 64 + (r & 63), column byte of kept value k at
+    // FT_COL + (k / 4) * 256 + (r & 63) * 4 + k % 4
+    auto buf = [&](int b) __attribute__((always_inline)) {
+      return b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3;
+    };
+    auto s_thr = [&](int r) __attribute__((always_inline)) -> float& {
+      return *reinterpret_cast<float*>(buf(r >> 6) + FT_TAIL + (r & 63) * 4);
+    };
+    auto s_cnt = [&](int r) __attribute__((always_inline)) -> int& {
+      return *reinterpret_cast<int*>(buf(r >> 6) + FT_TAIL + 256 + (r & 63) * 4);
+    };
+    __shared__ int s_over;
+    if (a.logits) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 64 + 16 * i + l16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int n = n0 + wn * 128 + 16 * j + 4 * g;
+          if (m < a.M && n < a.N)
+            *reinterpret_cast<f32x4*>(a.logits + (static_cast<int64_t>(m) * a.K + head) * a.N + n) = acc[i][j];
+        }
+      }
+    }
+    if (n0 + B2N > a.N) {  // columns past the vocabulary take no part
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n0 + wn * 128 + 16 * j + 4 * g + e >= a.N) acc[i][j][e] = -INFINITY;
+    }
+    // 1.
+    char* const wbuf = buf(wm);
+    const int sl = wn * 4 + g;
+    float gm[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float t1 = -INFINITY, t2 = -INFINITY, t3 = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 v = acc[i][j];
+        float x = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        x = x > -INFINITY ? x : -INFINITY;  // an all-NaN granule counts as empty
+        gm[i][j] = x;
+        t3 = fmaxf(t3, fminf(t2, x));
+        t2 = fmaxf(t2, fminf(t1, x));
+        t1 = fmaxf(t1, x);
+      }
+      *reinterpret_cast<f32x4*>(wbuf + sl * 1024 + (16 * i + l16) * 16) = f32x4{t1, t2, t3, -INFINITY};
+    }
+    if (tid < B2M) s_cnt(tid) = 0;
+    if (tid == 0) s_over = 0;
+    __syncthreads();
+    // 2. (threads 0..255 are waves 0..3: row tid sits in buffer `wave`)
+    if (tid < B2M) {
+      const char* rb = buf(wave) + (tid & 63) * 16;
+      float tl[KM];  // descending
+#pragma unroll
+      for (int s2 = 0; s2 < KM; ++s2) tl[s2] = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(rb + q * 1024);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          const float x = v[c];
+#pragma unroll
+          for (int s2 = KM - 1; s2 > 0; --s2) tl[s2] = __builtin_amdgcn_fmed3f(tl[s2 - 1], tl[s2], x);
+          tl[0] = fmaxf(tl[0], x);
+        }
+      }
+      float th = -INFINITY;
+#pragma unroll
+      for (int s2 = 0; s2 < KM; ++s2) th = s2 == a.kmax - 1 ? tl[s2] : th;
+      s_thr(tid) = fmaxf(th, -FLT_MAX);  // -inf logits (masked columns) never qualify
+    }
+    __syncthreads();
+    // 3.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = 16 * i + l16;
+      const float th = s_thr(wm * 64 + rl);
+      int n = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) n += gm[i][j] >= th ? 1 : 0;
+      int k = 0;
+      if (n) k = atomicAdd(&s_cnt(wm * 64 + rl), n);
+      if (k + n > FT_CAP) s_over = 1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (gm[i][j] >= th) {
+          if (k < FT_CAP) {
+            *reinterpret_cast<f32x4*>(wbuf + k * 1024 + rl * 16) = acc[i][j];
+            wbuf[FT_META + k * 64 + rl] = static_cast<char>(wn * 32 + 4 * j + g);
+          }
+          ++k;
+        }
+      }
+    }
+    __syncthreads();
+    if (!s_over) {
+      if (tid < B2M) {
+        char* rb = buf(wave);
+        const int rl = tid & 63;
+        const float th = s_thr(tid);
+        const int ng = s_cnt(tid);
+        // 4. four granules a round, their reads issued together.  Kept value
+        //    k goes to word k % 4 of granule slot k / 4, which is at most the
+        //    last slot read; its column byte to byte k % 4 of word k / 4 of
+        //    the column area.  Every value is written and the count moves on
+        //    only for a kept one, so the next write replaces a dropped value.
+        int k = 0;
+        for (int s = 0; s < ng; s += 4) {
+          f32x4 v[4];
+          int q[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int su = min(s + u, ng - 1);
+            v[u] = *reinterpret_cast<const f32x4*>(rb + su * 1024 + rl * 16);
+            q[u] = static_cast<unsigned char>(rb[FT_META + su * 64 + rl]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              *reinterpret_cast<float*>(rb + (k >> 2) * 1024 + rl * 16 + 4 * (k & 3)) = v[u][e];
+              rb[FT_COL + (k >> 2) * 256 + rl * 4 + (k & 3)] = static_cast<char>(4 * q[u] + e);
+              k += (s + u < ng && v[u][e] >= th) ? 1 : 0;
+            }
+          }
+        }
+        // 5. 64-bit keys: the value's bits in unsigned order above the
+        //    complemented column, so one unsigned compare ranks larger values
+        //    first and equal values by lower column (-0 taken as +0); key 0
+        //    is below every kept value
+        uint64_t tk[KM];
+#pragma unroll
+        for (int s2 = 0; s2 < KM; ++s2) tk[s2] = 0;
+        for (int c = 0; c < k; c += 4) {
+          const f32x4 x4 = *reinterpret_cast<const f32x4*>(rb + (c >> 2) * 1024 + rl * 16);
+          const uint32_t c4 = *reinterpret_cast<const uint32_t*>(rb + FT_COL + (c >> 2) * 256 + rl * 4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t bits = __float_as_uint(x4[u] + 0.0f);
+            const uint32_t ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+            const uint32_t col = static_cast<uint32_t>(n0) + ((c4 >> (8 * u)) & 0xffu);
+            uint64_t key = (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(~col);
+            if (c + u < k && key > tk[KM - 1]) {
+#pragma unroll
+              for (int s2 = 0; s2 < KM; ++s2) {  // keys are distinct: no tie to break
+                const bool take = key > tk[s2];
+                const uint64_t o = tk[s2];
+                tk[s2] = take ? key : o;
+                key = take ? o : key;
+              }
+            }
+          }
+        }
+        float tv[KM];
+        int ti[KM];
+#pragma unroll
+        for (int s2 = 0; s2 < KM; ++s2) {
+          const uint32_t ord = static_cast<uint32_t>(tk[s2] >> 32);
+          const uint32_t bits = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
+          tv[s2] = tk[s2] ? __uint_as_float(bits) : -INFINITY;
+          ti[s2] = tk[s2] ? static_cast<int>(~static_cast<uint32_t>(tk[s2])) : 0x7fffffff;
+        }
+        const int m = m0 + tid;
+        if (m < a.M) {
+          const int64_t base = ((static_cast<int64_t>(m) * a.K + head) * a.ntiles + nt) * a.kmax;
+#pragma unroll
+          for (int s2 = 0; s2 < KM; ++s2) {
+            if (s2 < a.kmax) {
+              a.cand_v[base + s2] = tv[s2];
+              a.cand_i[base + s2] = ti[s2];
+            }
+          }
+        }
+      }
+      return;
+    }
+
+    // ---- general epilogue (a row with many equal logits) -------------------
     // two passes of 128 rows; rows 32a .. 32a + 31 of a pass sit in stage
     // buffer a, column granule q (4 columns) of local row r at
     // (r % 32) * 1024 + 16 * (q ^ (r & 7))

@@ -130,6 +130,34 @@ def test_dense_ties_go_to_the_lower_index():
     assert (idx.cpu().numpy() == otopk.head_topk(lg, [6])).all()
 
 
+def test_dense_ties_large_tiles():
+    """256-row tiles (M = 256): a large duplicated vocab row makes equal
+    logits among each row's largest (within one 4-column granule, across
+    tiles and in the ragged last tile), so the tile's ranking must order
+    them by index whatever order they were gathered in; head 1 has one
+    all-zero 256-column tile, which takes the general ranking path while the
+    others do not."""
+    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=1, H=256, V=1000, K=2, topk=(10, 5), T=12,
+                                                  cfg_id=435)
+    hidden, w1, wlm = synth.head_inputs(w, DEV, M=256)
+    big = 4.0 * wlm[0, 17]
+    for c in (17, 18, 300, 640, 999):
+        wlm[0, c] = big
+    wlm[1, 256:512] = 0
+    t = _tree((10, 5), 12)
+    announce("dense heads ties, 256-row tiles")
+    _check(hidden, w1, wlm, t, (10, 5), TOL_BF16, round_r=True)
+    logits = torch.empty((256, 2, 1000), dtype=torch.float32, device=DEV)
+    idx, _ = api.heads_dense(hidden, w1, wlm, t, logits=logits)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert (lg[:, 0, 999] == lg[:, 0, 17]).all()
+    top = idx[:, 0].cpu().numpy()
+    pos = lg[:, 0, 17] >= lg[:, 0].max(axis=1)   # rows where the tied value is the largest
+    assert pos.sum() > 20
+    assert (top[pos, :5] == np.array([17, 18, 300, 640, 999])).all()
+
+
 @pytest.mark.parametrize("name", ["vicuna7b-shaped", "vicuna13b-shaped", "vicuna33b-shaped", "zephyr7b-shaped"])
 def test_dense_full_size(name):
     """M = B*T rows at the workload's shape; the oracle recomputes sampled
