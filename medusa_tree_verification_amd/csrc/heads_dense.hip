@@ -871,6 +871,89 @@ __global__ __launch_bounds__(256) void dense_topk_merge(MergeArgs a) {
   }
 }
 
+// ---- final merge of sorted tile lists: a tournament -------------------------
+// One wave per (row m, head d).  The pair's tile lists (each sorted: larger
+// logit first, equal logits by lower column) are copied to LDS; lane L
+// follows lists L, L + 64, ... with a cursor each.  Every round takes the
+// wave-wide arg-max of the lanes' best list heads (ties to the lower index),
+// and only the winning list moves on, so a round costs one arg-max and one
+// LDS read rather than insertions into every lane's list.
+constexpr int TOURNEY_LPL = 4;  // lists per lane: up to 256 lists
+__global__ __launch_bounds__(64) void dense_topk_tourney(MergeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char tl_lds[];
+  const int row = blockIdx.x;  // = m * K + d; the grid is M * K
+  const int lane = threadIdx.x;
+  const int n = a.nlist * a.kmax;
+  float* sv = reinterpret_cast<float*>(tl_lds);
+  int* si = reinterpret_cast<int*>(tl_lds + ((n * 4 + 15) & ~15));
+  const float* v = a.v + static_cast<int64_t>(row) * n;
+  const int32_t* ix = a.ix + static_cast<int64_t>(row) * n;
+  // 16 loads per lane in flight at once: the lists were just written by
+  // workgroups on other XCDs, so every read is a trip to memory
+  constexpr int U = 16;
+  for (int e0 = 0; e0 < n; e0 += 64 * U) {
+    float xv[U];
+    int xi[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int e = e0 + lane + 64 * q;
+      xv[q] = e < n ? v[e] : 0.f;
+      xi[q] = e < n ? ix[e] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int e = e0 + lane + 64 * q;
+      if (e < n) {
+        sv[e] = xv[q];
+        si[e] = xi[q];
+      }
+    }
+  }
+  __syncthreads();
+  float hv[TOURNEY_LPL];
+  int hi[TOURNEY_LPL], cur[TOURNEY_LPL];
+#pragma unroll
+  for (int u = 0; u < TOURNEY_LPL; ++u) {
+    const int l = lane + 64 * u;
+    const bool in = l < a.nlist;
+    const int e = in ? l * a.kmax : 0;  // every read in range
+    cur[u] = 0;
+    hv[u] = in ? sv[e] : -INFINITY;
+    hi[u] = in ? si[e] : 0x7fffffff;
+  }
+  const int kd = a.kpd[row % a.K];
+  int32_t* oi = a.out_idx + static_cast<int64_t>(row) * a.kmax_out;
+  float* ov = a.out_val ? a.out_val + static_cast<int64_t>(row) * a.kmax_out : nullptr;
+  for (int s = 0; s < a.kmax_out; ++s) {
+    if (s >= kd) {
+      if (lane == 0) {
+        oi[s] = -1;
+        if (ov) ov[s] = 0.f;
+      }
+      continue;
+    }
+    float bv = hv[0];
+    int bi = hi[0];
+#pragma unroll
+    for (int u = 1; u < TOURNEY_LPL; ++u) best_of(bv, bi, hv[u], hi[u]);
+    wave_best(bv, bi);
+    if (lane == 0) {
+      oi[s] = bi;
+      if (ov) ov[s] = bv;
+    }
+#pragma unroll
+    for (int u = 0; u < TOURNEY_LPL; ++u) {
+      if (hv[u] == bv && hi[u] == bi) {  // indices are distinct: one list moves on
+        const int l = lane + 64 * u;
+        const bool more = l < a.nlist && ++cur[u] < a.kmax;
+        const int e = more ? l * a.kmax + cur[u] : 0;
+        hv[u] = more ? sv[e] : -INFINITY;
+        hi[u] = more ? si[e] : 0x7fffffff;
+      }
+    }
+  }
+}
+
 // ---- fp32: plain VALU products (small configurations) ---------------------
 struct DenseF32Args {
   const float* x;  // [M][H] hidden, or r [K][M][H]
@@ -990,8 +1073,18 @@ int launch_topk_big(const DenseArgs& a, int KM, hipStream_t s) {
   }
 }
 
+size_t tourney_lds(const MergeArgs& a) {
+  const size_t n = static_cast<size_t>(a.nlist) * a.kmax;
+  return round_up(n * 4, 16) + n * 4;
+}
+
 template <bool LISTS>
 int launch_merge(const MergeArgs& a, int KM, hipStream_t s) {
+  if (LISTS && a.nlist <= 64 * TOURNEY_LPL && tourney_lds(a) <= 64 * 1024) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.M) * a.K));
+    hipLaunchKernelGGL(dense_topk_tourney, grid, dim3(64), tourney_lds(a), s, a);
+    return check_launch("dense heads top-k merge");
+  }
   const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(a.M) * a.K + 3) / 4));
   switch (KM) {
     case 4: hipLaunchKernelGGL((dense_topk_merge<4, LISTS>), grid, dim3(256), 0, s, a); break;
