@@ -443,7 +443,10 @@ def main():
     attn_total = stages_us["attention"]
     dominant_attention = attn_total >= stages_us["heads"]
     if dominant_attention:
-        roof = {"kernel": "tree attention, one layer (tree_attn_bf16 + merge_splits)", "bound": "hbm",
+        # more than 128 query rows per K/V head (T x query heads per K/V head)
+        # run the grouped-query kernel
+        attn_kernel = "tree_attn_gqa" if (w.Hq // w.Hkv) * w.T > 128 else "tree_attn_bf16"
+        roof = {"kernel": f"tree attention, one layer ({attn_kernel} + merge_splits)", "bound": "hbm",
                 "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                 "traffic": counter_traffic(w, "tree_attention", "attention.hip"),
