@@ -618,6 +618,70 @@ __global__ __launch_bounds__(64) void merge_splits(AttnArgs a) {
   *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv));
 }
 
+// The same merge with 16-byte pieces: four rows per wave, 16 lanes per row,
+// 8 consecutive d per lane (NS <= 64: lane s holds splits s, s + 16, ...).
+__global__ __launch_bounds__(64) void merge_splits16(AttnArgs a) {
+  const int lane = threadIdx.x & 15;  // lane within the row's 16
+  const int BH = a.B * a.Hkv;
+  const int64_t gr = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 4);
+  const bool live = gr < static_cast<int64_t>(a.L) * BH * a.QR;  // every row group reaches the shuffles
+  const int64_t grc = live ? gr : 0;
+  const int lbh = static_cast<int>(grc / a.QR);
+  const int bh = lbh % BH, layer = lbh / BH;
+  const int r = static_cast<int>(grc % a.QR);
+  const int64_t stride = static_cast<int64_t>(a.L) * BH * a.QRpad;
+  const int64_t row = static_cast<int64_t>(lbh) * a.QRpad + r;
+  const int ns = a.NS;
+  float2 ml[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int sp = lane + 16 * q;
+    ml[q] = sp < ns ? *reinterpret_cast<const float2*>(a.part_ml + (row * ns + sp) * 2) : make_float2(-INFINITY, 0.f);
+  }
+  uint4 ov[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    ov[u] = (u < ns) ? *reinterpret_cast<const uint4*>(a.part_o + (u * stride + row) * D + 8 * lane)
+                     : make_uint4(0, 0, 0, 0);
+  float M = fmaxf(fmaxf(ml[0].x, ml[1].x), fmaxf(ml[2].x, ml[3].x));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
+  const float muse = (M == -INFINITY) ? 0.f : M;
+  float w[4], L = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    w[q] = __builtin_amdgcn_exp2f(ml[q].x - muse) * ml[q].y;
+    L += w[q];
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) L += __shfl_xor(L, off, 16);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](uint4 v, float wu) __attribute__((always_inline)) {
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(bf16_bits_to_f32(p[e] & 0xffffu), wu, acc[2 * e]);
+      acc[2 * e + 1] = fmaf(bf16_bits_to_f32(p[e] >> 16), wu, acc[2 * e + 1]);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (u < ns) add(ov[u], __shfl(w[0], u, 16));
+  for (int s_ = 16; s_ < ns; ++s_) {
+    const uint4 v = *reinterpret_cast<const uint4*>(a.part_o + (s_ * stride + row) * D + 8 * lane);
+    const float ws = s_ < 32 ? w[1] : (s_ < 48 ? w[2] : w[3]);
+    add(v, __shfl(ws, s_ & 15, 16));
+  }
+  if (!live) return;
+  const float inv = 1.0f / L;
+  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
+  const int node = r / a.G, gq = r % a.G;
+  uint16_t* op = a.out + layer * a.out_lstride +
+                 ((static_cast<int64_t>(b) * a.T + node) * a.Hq + kvh * a.G + gq) * D + 8 * lane;
+  *reinterpret_cast<uint4*>(op) = make_uint4(pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv),
+                                             pack_bf16(acc[4] * inv, acc[5] * inv), pack_bf16(acc[6] * inv, acc[7] * inv));
+}
+
 // ---- grouped-query shapes: every query row of a K/V head in one workgroup ----
 // For more than 128 query rows per K/V head (T * G, e.g. 64 nodes x 4 query
 // heads) the rows no longer fit the two-role kernel above without a second
@@ -1280,8 +1344,14 @@ int attention_launch(const void* q, const void* k_cache, const void* v_cache, in
   }
   if (rc || p.NS == 1) return rc;
   const int64_t rows = static_cast<int64_t>(L) * B * Hkv * p.QR;
-  // one wave (two rows) per workgroup: measured faster than 4 or 16 waves
-  hipLaunchKernelGGL(merge_splits, dim3(static_cast<unsigned>((rows + 1) / 2)), dim3(64), 0, stream, a);
+  // one wave per workgroup (measured faster than 4 or 16 waves); with 4096
+  // rows or more, four rows per wave in 16-byte pieces (zephyr7b-shaped: a
+  // layer's call ~4.5 us shorter), below that two rows per wave in 8-byte
+  // pieces (more waves for few rows)
+  if (rows >= 4096)
+    hipLaunchKernelGGL(merge_splits16, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(merge_splits, dim3(static_cast<unsigned>((rows + 1) / 2)), dim3(64), 0, stream, a);
   return check_launch("tree attention split merge");
 }
 

@@ -143,15 +143,18 @@ def test_attention_full_size_sampled_rows(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 4), (32, 16)])
 @pytest.mark.parametrize("splits", [19, 63])
-def test_attention_many_splits(splits, monkeypatch):
-    """Many splits per (sequence, head), repeated on one workspace."""
-    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=2, Hq=8, Hkv=4, ctx=4100, cfg_id=235)
+def test_attention_many_splits(splits, hq, hkv, monkeypatch):
+    """Many splits per (sequence, head), repeated on one workspace; 1024 and
+    4096 query rows (the split merge takes 8-byte pieces below 4096 rows and
+    16-byte pieces from there)."""
+    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(B=2, Hq=hq, Hkv=hkv, ctx=4100, cfg_id=235)
     parent, rank = synth.cost_ordered_tree(w.topk, w.T)
     t = api.Tree(parent, rank, w.topk)
     q, k, v, ctx = synth.attention_inputs(w, 0, DEV, ctx_lens=[4100, 2600])
     monkeypatch.setenv("MEDUSA_ATTN_SPLITS", str(splits))
-    announce("attention many splits", splits)
+    announce("attention many splits", splits, "heads", hq, hkv)
     nb = api.tree_attention_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.ctx, t, torch.bfloat16)
     ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
     ref = _oracle_full(q, k, v, ctx.tolist(), parent)
