@@ -76,9 +76,14 @@ struct DenseArgs {
   float* logits;        // optional [M][K][N]
 };
 
-template <int BM, int EPI, int KM, int BNT = BN>
-__global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
+// KG k-groups of 4 waves: group q takes k-steps q, q + KG, ... with its own
+// LDS buffers, and the groups' sums meet in LDS before the epilogue, so a
+// workgroup keeps KG times the loads in flight (the residual block at small M
+// has one workgroup per CU and is bound by the bytes on their way).
+template <int BM, int EPI, int KM, int BNT = BN, int KG = 1>
+__global__ __launch_bounds__(256 * KG) void dense_gemm_bf16(DenseArgs a) {
   static_assert(BNT == BN || EPI == EPI_RESID, "the top-k epilogue takes 128-column tiles");
+  static_assert(KG == 1 || EPI == EPI_RESID, "k-groups only in front of the residual epilogue");
   constexpr int MT = BM / 32;         // 16-row activation tiles per wave
   constexpr int NJ = BNT / 32;        // 16-column output tiles per wave
   constexpr int XCH = BM * 8 / 256;   // 16-byte X chunks per thread per step
@@ -98,7 +103,9 @@ __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
   const int m0 = mt * BM, n0 = nt * BNT;
   if (m0 >= a.M || n0 >= a.N) return;  // no tile past the matrices (whole workgroup, no barrier yet)
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x & 255;
+  const int kg = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 8);
+  char* const sm = smem + kg * 2 * STAGE;  // this k-group's two buffers
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
     loff[u] = (isx ? 0 : XT) + toff(c >> 3, c & 7);
   }
   auto gload = [&](uint4 (&R)[CH], int ks) __attribute__((always_inline)) {
-    const int kb = ks * TROW;
+    const int kb = (ks * KG + kg) * TROW;  // this group's ks-th k-step
 #pragma unroll
     for (int u = 0; u < CH; ++u) R[u] = bload16(u < XCH ? rx : rw, goff[u] + kb);
   };
@@ -159,26 +166,46 @@ __global__ __launch_bounds__(256) void dense_gemm_bf16(DenseArgs a) {
   };
 
   // Pipeline: block b is in registers R[b & 1] until it is written to LDS
-  // buffer b & 1 during step b - 1; nk is even, so the unrolled pair of steps
-  // keeps every register index a constant.  Loads of blocks past the end
-  // read zeros or bytes of the next row and are never used.
-  const int nk = a.Kd / BK;
+  // buffer b & 1 during step b - 1; a group's step count is even, so the
+  // unrolled pair of steps keeps every register index a constant.  Loads of
+  // blocks past the end read zeros or bytes of the next row and are never
+  // used.
+  const int nk = a.Kd / BK / KG;
   uint4 R[2][CH];
   gload(R[0], 0);
   __builtin_amdgcn_sched_barrier(0);
   gload(R[1], 1);
   __builtin_amdgcn_sched_barrier(0);
-  lput(R[0], smem);
+  lput(R[0], sm);
   gload(R[0], 2);
   __syncthreads();
   for (int ks = 0; ks < nk; ks += 2) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      compute(smem + j * STAGE);
-      lput(R[(j + 1) & 1], smem + ((j + 1) & 1) * STAGE);
+      compute(sm + j * STAGE);
+      lput(R[(j + 1) & 1], sm + ((j + 1) & 1) * STAGE);
       gload(R[(j + 1) & 1], ks + j + 3);
       __syncthreads();
     }
+  }
+  if constexpr (KG == 2) {
+    // the second group's sums into its own buffers (the loop's last barrier
+    // ended every read of them), then added by the first group in k-group
+    // order; the second group leaves (no barrier follows in its epilogue)
+    static_assert(MT * NJ * 256 * 16 <= 2 * STAGE, "k-group sums exceed the group's buffers");
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(sm + ((i * NJ + j) * 256 + tid) * 16) = acc[i][j];
+    }
+    __syncthreads();
+    if (kg == 1) return;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] += *reinterpret_cast<const f32x4*>(smem + 2 * STAGE + ((i * NJ + j) * 256 + tid) * 16);
   }
 
   if constexpr (EPI == EPI_RESID) {
@@ -1028,12 +1055,12 @@ constexpr int dense_lds() {
   return stage > tile ? (stage > lists ? stage : lists) : (tile > lists ? tile : lists);
 }
 
-template <int BM, int EPI, int KM, int BNT = BN>
+template <int BM, int EPI, int KM, int BNT = BN, int KG = 1>
 int launch_gemm(const DenseArgs& a, hipStream_t s, const char* what) {
-  constexpr int lds = dense_lds<BM, EPI, KM, BNT>();
+  constexpr int lds = KG * dense_lds<BM, EPI, KM, BNT>();
   static_assert(lds <= 64 * 1024, "dense heads LDS above the default limit");
   const int grid = 8 * a.per_xcd;
-  hipLaunchKernelGGL((dense_gemm_bf16<BM, EPI, KM, BNT>), dim3(grid), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((dense_gemm_bf16<BM, EPI, KM, BNT, KG>), dim3(grid), dim3(256 * KG), lds, s, a);
   return check_launch(what);
 }
 
@@ -1199,6 +1226,8 @@ extern "C" int medusa_heads_dense(const void* hidden, const void* w1, int64_t w1
   a.hid = static_cast<const uint16_t*>(hidden);
   a.r_out = reinterpret_cast<uint16_t*>(w);
   if (p.big) rc = launch_big<EPI_RESID, 4>(a, stream, "dense heads residual block (256 x 256 tiles)");
+  else if (p.BM == 64 && (H / BK) % 4 == 0)  // two k-groups: each an even number of k-steps
+    rc = launch_gemm<64, EPI_RESID, 4, RBN, 2>(a, stream, "dense heads residual block");
   else if (p.BM == 64) rc = launch_gemm<64, EPI_RESID, 4, RBN>(a, stream, "dense heads residual block");
   else rc = launch_gemm<128, EPI_RESID, 4, RBN>(a, stream, "dense heads residual block");
   if (rc) return rc;
