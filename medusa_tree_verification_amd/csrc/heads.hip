@@ -66,36 +66,44 @@ __device__ __forceinline__ void load_chunk(Chunk<CH>& c, const uint16_t* p, int 
   }
 }
 
-template <int NT, int CH>
-__device__ __forceinline__ void mfma_chunk(f32x4 (&acc)[NT], const Chunk<CH>& w,
+template <int RT, int NT, int CH>
+__device__ __forceinline__ void mfma_chunk(f32x4 (&acc)[RT][NT], const Chunk<CH> (&w)[RT],
                                            const Chunk<CH> (&x)[NT]) {
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w.v[j]), as_bf16x8(x[t].v[j]),
-                                                        acc[t], 0, 0, 0);
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[rt].v[j]), as_bf16x8(x[t].v[j]),
+                                                              acc[rt][t], 0, 0, 0);
   }
 }
 
 constexpr int XPAD = 8;              // LDS row padding of the staged activations (elements)
 constexpr int XLDS_MAX = 64 * 1024;  // largest activation block staged in LDS (more costs occupancy)
 
-// grid: (ceil(R/16), G, passes); block: 256 (4 waves on the same 16 rows)
-template <int NT, int EPI, bool XLDS>
+// grid: (ceil(R/(16 RT)), G, passes); block: 256 (4 waves on the same 16 RT
+// rows).  RT = 2 when the activation rows come from L2 (too large to stage):
+// each of their loads then serves 32 weight rows instead of 16.
+template <int NT, int EPI, bool XLDS, int RT = 1>
 __global__ __launch_bounds__(256) void skinny_gemm_bf16(GemmArgs a) {
-  constexpr int CH = (NT == 1) ? 8 : 4;  // MFMA k-steps (16-byte loads per lane) per chunk
-  constexpr int STEP = 32 * CH;          // elements per chunk
+  constexpr int CH = (NT == 1 && RT == 1) ? 8 : 4;  // MFMA k-steps (16-byte loads per lane) per chunk
+  constexpr int STEP = 32 * CH;                     // elements per chunk
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = blockIdx.y;
   const int n0 = blockIdx.z * NT * 16;
-  const int row0 = blockIdx.x * 16;
+  const int row0 = blockIdx.x * 16 * RT;
   const int nl = min(NT * 16, a.N - n0);  // activation rows of this pass
-  const int rl = min(row0 + (lane & 15), a.R - 1);
   const int kq = (lane >> 4) * 8;
-  const uint16_t* wp = a.W + g * a.w_gstride + static_cast<int64_t>(rl) * a.Kd + kq;
+  const uint16_t* wp[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rl = min(row0 + 16 * rt + (lane & 15), a.R - 1);
+    wp[rt] = a.W + g * a.w_gstride + static_cast<int64_t>(rl) * a.Kd + kq;
+  }
   const uint16_t* xg = a.X + g * a.x_gstride + static_cast<int64_t>(n0) * a.Kd;
   const int xrow = a.Kd + XPAD;
   uint16_t* sx = reinterpret_cast<uint16_t*>(smem);
@@ -115,15 +123,18 @@ __global__ __launch_bounds__(256) void skinny_gemm_bf16(GemmArgs a) {
     const int n = t * 16 + (lane & 15);
     xo[t] = n < nl ? (XLDS ? n * xrow : n * a.Kd) + kq : -1;
   }
-  f32x4 acc[NT];
+  f32x4 acc[RT][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nchunks = (a.Kd + STEP - 1) / STEP;
-  Chunk<CH> wa, wb, xa[NT], xb[NT];
-  auto load = [&](Chunk<CH>& w, Chunk<CH>(&x)[NT], int c) __attribute__((always_inline)) {
+  Chunk<CH> wa[RT], wb[RT], xa[NT], xb[NT];
+  auto load = [&](Chunk<CH>(&w)[RT], Chunk<CH>(&x)[NT], int c) __attribute__((always_inline)) {
     const int avail = a.Kd - c * STEP - kq;
-    load_chunk<CH>(w, wp + static_cast<int64_t>(c) * STEP, avail);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) load_chunk<CH>(w[rt], wp[rt] + static_cast<int64_t>(c) * STEP, avail);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (xo[t] < 0) {
@@ -144,51 +155,60 @@ __global__ __launch_bounds__(256) void skinny_gemm_bf16(GemmArgs a) {
   if (c < nchunks) load(wa, xa, c);
   for (; c + 4 < nchunks; c += 8) {
     load(wb, xb, c + 4);
-    mfma_chunk<NT, CH>(acc, wa, xa);
+    mfma_chunk<RT, NT, CH>(acc, wa, xa);
     if (c + 8 < nchunks) load(wa, xa, c + 8);
-    mfma_chunk<NT, CH>(acc, wb, xb);
+    mfma_chunk<RT, NT, CH>(acc, wb, xb);
   }
-  if (c < nchunks) mfma_chunk<NT, CH>(acc, wa, xa);
+  if (c < nchunks) mfma_chunk<RT, NT, CH>(acc, wa, xa);
 
   // waves 1-3 hand their partial sums to wave 0 (added in wave order)
   f32x4* red = reinterpret_cast<f32x4*>(smem + (XLDS ? round_up16(nl * xrow * 2) : 0));
   if (wave > 0) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) red[((wave - 1) * NT + t) * 64 + lane] = acc[t];
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) red[(((wave - 1) * RT + rt) * NT + t) * 64 + lane] = acc[rt][t];
   }
   __syncthreads();
   if (wave > 0) return;
 #pragma unroll
   for (int w = 0; w < 3; ++w)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] += red[(w * NT + t) * 64 + lane];
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[rt][t] += red[((w * RT + rt) * NT + t) * 64 + lane];
 
-  // C layout: lane holds column (lane & 15) and rows 4*(lane >> 4) + e
-  const int rbase = row0 + 4 * (lane >> 4);
+  // C layout: lane holds column (lane & 15) and rows 4*(lane >> 4) + e of
+  // each 16-row tile
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int n = n0 + t * 16 + (lane & 15);
-    if (n >= a.N) continue;
-    if (EPI == EPI_RESID) {
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rbase = row0 + 16 * rt + 4 * (lane >> 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int r = rbase + e;
-        if (r >= a.R) break;
-        float y = acc[t][e];
-        float s = y / (1.0f + expf(-y));
-        float h = bf16_bits_to_f32(a.hid[static_cast<int64_t>(n) * a.R + r]);
-        a.out_r[static_cast<int64_t>(g) * a.N * a.R + static_cast<int64_t>(n) * a.R + r] =
-            static_cast<uint16_t>(f32_to_bf16_bits(s + h));
-      }
-    } else {
-      float* dst = a.logits + static_cast<int64_t>(n % a.M) * a.stride_m +
-                   static_cast<int64_t>(g + n / a.M) * a.V + rbase;
-      if (rbase + 3 < a.R && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+    for (int t = 0; t < NT; ++t) {
+      const int n = n0 + t * 16 + (lane & 15);
+      if (n >= a.N) continue;
+      if (EPI == EPI_RESID) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int r = rbase + e;
+          if (r >= a.R) break;
+          float y = acc[rt][t][e];
+          float s = y / (1.0f + expf(-y));
+          float h = bf16_bits_to_f32(a.hid[static_cast<int64_t>(n) * a.R + r]);
+          a.out_r[static_cast<int64_t>(g) * a.N * a.R + static_cast<int64_t>(n) * a.R + r] =
+              static_cast<uint16_t>(f32_to_bf16_bits(s + h));
+        }
       } else {
+        float* dst = a.logits + static_cast<int64_t>(n % a.M) * a.stride_m +
+                     static_cast<int64_t>(g + n / a.M) * a.V + rbase;
+        if (rbase + 3 < a.R && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          *reinterpret_cast<float4*>(dst) =
+              make_float4(acc[rt][t][0], acc[rt][t][1], acc[rt][t][2], acc[rt][t][3]);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (rbase + e < a.R) dst[e] = acc[t][e];
+          for (int e = 0; e < 4; ++e)
+            if (rbase + e < a.R) dst[e] = acc[rt][t][e];
+        }
       }
     }
   }
@@ -273,6 +293,11 @@ int launch_nt(const GemmArgs& a, int G, hipStream_t s) {
       }
     }
     hipLaunchKernelGGL((skinny_gemm_bf16<NT, EPI, true>), grid, dim3(256), lds, s, a);
+  } else if constexpr (NT <= 2) {
+    // activation rows from L2: two 16-row weight tiles per workgroup (with
+    // more column tiles the registers would not hold two)
+    const dim3 grid2((a.R + 31) / 32, G, grid.z);
+    hipLaunchKernelGGL((skinny_gemm_bf16<NT, EPI, false, 2>), grid2, dim3(256), 2 * red, s, a);
   } else {
     hipLaunchKernelGGL((skinny_gemm_bf16<NT, EPI, false>), grid, dim3(256), red, s, a);
   }

@@ -41,6 +41,9 @@ SMALL_BF16 = [
     (4, 512, 1500, 5, True),        # shared lm_head: 20 columns in one pass
     (70, 128, 200, 1, False),       # several column passes
     (2, 264, 333, 3, False),        # H not a multiple of the 256-element chunk
+    # 8 activation rows of 4104 do not fit the LDS staging: two 16-row weight
+    # tiles per workgroup, with ragged ends at R = 4104 and R = 1001
+    (8, 4104, 1001, 2, False),
 ]
 
 
