@@ -98,6 +98,9 @@ SMALL = [
     ("m16-shared", 16, 128, 512, (4, 4), True),
     ("m130-k32", 130, 128, 640, (32, 8), False),
     ("m1-k1", 1, 128, 256, (1, 1, 1), False),
+    # 256-row tiles: rows past M in the second row tile, one ragged column
+    # tile of 200, a head keeping one candidate next to one keeping twelve
+    ("m300-v200", 300, 128, 200, (12, 1), False),
     # 313 tile lists per (row, head): more than the merge's 256 staged lists
     ("m16-v40000", 16, 128, 40000, (10, 4), False),
 ]
