@@ -927,17 +927,24 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
                          pack_bf16(p[1][2], p[1][3]));
     }
   };
-  // O^T += V^T P^T over the half's 32 keys
+  // O^T += V^T P^T over the half's 32 keys.  All 16 transposing reads of the
+  // half are issued before the first MFMA uses them, so their latencies
+  // overlap (read one pair, wait, multiply left each wave with eight
+  // LDS round trips in a row).
   auto pv = [&](const char* blk, int h, const uint4 (&pb)[GQ_TILES]) __attribute__((always_inline)) {
+    uint2 lo[8], hi[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const char* vp = blk + (vx0 ^ (32 * dt)) + 32 * h * GROWB;
+      lo[dt] = lds_read_tr(vp);
+      hi[dt] = lds_read_tr(vp + 16 * GROWB);
+    }
 #pragma unroll
     for (int t = 0; t < GQ_TILES; ++t)
       lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pb[t]), lsum[t], 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const char* vp = blk + (vx0 ^ (32 * dt)) + 32 * h * GROWB;
-      const uint2 lo = lds_read_tr(vp);
-      const uint2 hi = lds_read_tr(vp + 16 * GROWB);
-      const bf16x8 va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const bf16x8 va = as_bf16x8(make_uint4(lo[dt].x, lo[dt].y, hi[dt].x, hi[dt].y));
 #pragma unroll
       for (int t = 0; t < GQ_TILES; ++t)
         o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(pb[t]), o[t][dt], 0, 0, 0);
