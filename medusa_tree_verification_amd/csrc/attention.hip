@@ -736,6 +736,7 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
 __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char s0[GQ_SLOT], s1[GQ_SLOT], s2[GQ_SLOT], s3[GQ_SLOT];
   __shared__ uint64_t smask[GQ_MASK_WORDS];
+  __shared__ int s_redo;
   const int id = blockIdx.x;
   const int task = (id & 7) * a.per_xcd + (id >> 3);
   if (task >= a.tasks) return;  // whole workgroup leaves before any barrier
@@ -751,6 +752,7 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
   uint16_t* outL = a.out + layer * a.out_lstride;
 
   const int tid = threadIdx.x;
+  if (tid == 0) s_redo = 0;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
@@ -826,14 +828,17 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
   // (as bf16, the values P.V uses), accumulated by an MFMA against ones
   f32x4 lsum[GQ_TILES];
   float m_run[GQ_TILES], mu[GQ_TILES];
+  auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int t = 0; t < GQ_TILES; ++t) {
-    m_run[t] = -INFINITY;
-    mu[t] = 0.f;
-    lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < GQ_TILES; ++t) {
+      m_run[t] = -INFINITY;
+      mu[t] = 0.f;
+      lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+      for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  reset();
   const bf16x8 ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
   // K row kt * 16 + l16, chunk 4s + grp sits at kx0 ^ 64 s in the row
   const int kx0 = 16 * (grp ^ l16);
@@ -957,8 +962,10 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
   // short software pipeline whose MFMA and VALU parts are independent: the
   // second half's scores next to the first half's exponentials, the first
   // half's P.V next to the second half's exponentials.  A rescale at the
-  // second half also rescales the first half's waiting P^T.
-  auto step = [&](char* cur, char* ahead, int i) __attribute__((always_inline)) {
+  // second half also rescales the first half's waiting P^T.  With checks
+  // off the block's probabilities are taken against the reference as it
+  // stands, however far its scores rise above it (see the pass below).
+  auto step = [&](char* cur, char* ahead, int i, bool checks) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
@@ -970,7 +977,7 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
       uint4 pb0[GQ_TILES], pb1[GQ_TILES];
       qk_mma(cur, 0, sc0);
       qk_mask(kb0, sc0);
-      pre(sc0, nullptr);
+      if (checks) pre(sc0, nullptr);
       // second half's scores (16 MFMAs) beside the first half's exponentials
       qk_mma(cur, 1, sc1);
       expo(sc0, pb0);
@@ -980,7 +987,7 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
       qk_mask(kb0 + 32, sc1);
-      pre(sc1, pb0);
+      if (checks) pre(sc1, pb0);
       // first half's P.V (18 MFMAs) beside the second half's exponentials
       pv(cur, 0, pb0);
       expo(sc1, pb1);
@@ -992,14 +999,48 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
       pv(cur, 1, pb1);
     }
   };
-  for (int i = 0; i < nblk; i += 4) {
-    step(s0, s2, i);
-    step(s1, s3, i + 1);
-    step(s2, s0, i + 2);
-    step(s3, s1, i + 3);
+  // First pass: the reference max is checked in the split's first block
+  // only and then held, which takes the per-half maxima and their vote off
+  // the vector unit.  Softmax does not depend on the reference, so the
+  // result is the same wherever the probabilities stay in range.  They do
+  // unless a later key's score exceeds the first block's maximum by a wide
+  // margin: the pass is kept if every row's running sum is at most 2^64 and
+  // every output accumulator is finite (then no probability, sum or product
+  // overflowed, and the merge's weights exp2(m - M) l keep their range), and
+  // if every row saw a key in the first block (else its reference is a
+  // placeholder that later probabilities could underflow against).  If any
+  // wave fails, the workgroup computes the split again checking every half,
+  // the reference then following the running maximum within RESCALE_SLACK.
+  bool exact = false;
+  for (;;) {
+    for (int i = 0; i < nblk; i += 4) {
+      step(s0, s2, i, exact || i == 0);
+      step(s1, s3, i + 1, exact);
+      step(s2, s0, i + 2, exact);
+      step(s3, s1, i + 3, exact);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // every load (also those past the split) has landed
+    __syncthreads();
+    if (exact) break;
+    bool bad = false;
+#pragma unroll
+    for (int t = 0; t < GQ_TILES; ++t) {
+      float mag = 0.f;  // inf and NaN carry through the sum
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mag += fabsf(o[t][dt][e]);
+      const bool live = row0 + t * 16 + l16 < a.QR;  // padding rows repeat a row under the root's mask
+      bad |= live && (!(lsum[t][0] <= 0x1p64f) || !(mag <= 3.0e38f) || (nblk > 0 && m_run[t] == -INFINITY));
+    }
+    if (__builtin_amdgcn_ballot_w64(bad)) s_redo = 1;
+    __syncthreads();
+    if (!s_redo) break;
+    exact = true;
+    reset();
+    gload(s0, 0);
+    gload(s1, 1);
   }
-  __builtin_amdgcn_s_waitcnt(0x0070);  // every load (also those past the split) has landed
-  __syncthreads();
 
   float l_run[GQ_TILES];
 #pragma unroll

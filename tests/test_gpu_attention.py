@@ -164,6 +164,54 @@ def test_attention_many_splits(splits, hq, hkv, monkeypatch):
         assert row_rel_err(to64(out), ref) <= TOL_BF16, rep
 
 
+def _excess_over_first_block(q, k, ctx, G):
+    """Per query row (context keys only, every row sees them): how far, in
+    log2 units of the softmax, the largest score lies above the largest
+    score among the first 64 keys."""
+    qn, kn = to64(q), to64(k)
+    c = (1 / np.sqrt(qn.shape[-1])) / np.log(2)
+    out = []
+    for b in range(qn.shape[0]):
+        n = int(ctx[b])
+        for h in range(qn.shape[2]):
+            s = qn[b, :, h] @ kn[b, h // G, :n].T * c
+            out.append(s.max(axis=1) - s[:, :64].max(axis=1))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("kind,f", [("kept", 6.0), ("redo", 48.0)])
+def test_attention_gqa_rising_scores(kind, f, splits, monkeypatch):
+    """The one-workgroup-per-K/V-head kernel (4 query heads per K/V head,
+    64 nodes) on keys whose scale grows along the sequence, so that later
+    scores rise far above those of a split's first block.  'kept': by more
+    than the slack at which the reference max is otherwise moved, but with
+    every probability far below overflow, so the first pass stands with
+    probabilities up to ~2^37; 'redo': by more than 128, so the first pass
+    overflows and the split is computed again checking every half.  The
+    inputs are checked on the CPU to have that property."""
+    w = synth.WORKLOADS["zephyr7b-shaped"].scaled(B=2, ctx=2000, cfg_id=241)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    t = api.Tree(parent, rank, w.topk)
+    q, k, v, ctx = synth.attention_inputs(w, 0, DEV, ctx_lens=[2000, 1937])
+    ramp = 1 + (f - 1) * torch.arange(k.shape[2], device=DEV, dtype=torch.float32) / k.shape[2]
+    k = (k.float() * ramp[None, None, :, None]).to(torch.bfloat16).contiguous()
+    ex = _excess_over_first_block(q, k, ctx.tolist(), w.Hq // w.Hkv)
+    if kind == "kept":
+        assert ex.min() >= 8 and ex.max() <= 45, (ex.min(), ex.max())
+    else:
+        assert ex.max() >= 130, ex.max()
+    monkeypatch.setenv("MEDUSA_ATTN_SPLITS", str(splits))
+    announce("attention gqa rising scores", kind, "splits", splits)
+    out = api.tree_attention(q, k, v, ctx, w.ctx, t)
+    torch.cuda.synchronize()
+    ref = _oracle_full(q, k, v, ctx.tolist(), parent)
+    got = to64(out)
+    assert np.all(np.isfinite(got))
+    err = row_rel_err(got, ref)
+    assert err <= TOL_BF16, err
+
+
 def test_attention_deterministic():
     w = synth.WORKLOADS["zephyr7b-shaped"].scaled(B=2, ctx=1000, cfg_id=240)
     parent, rank = synth.cost_ordered_tree(w.topk, w.T)
