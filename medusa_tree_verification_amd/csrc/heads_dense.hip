@@ -906,30 +906,32 @@ __global__ __launch_bounds__(256) void dense_topk_merge(MergeArgs a) {
 // and only the winning list moves on, so a round costs one arg-max and one
 // LDS read rather than insertions into every lane's list.
 constexpr int TOURNEY_LPL = 4;  // lists per lane: up to 256 lists
-__global__ __launch_bounds__(64) void dense_topk_tourney(MergeArgs a) {
+__global__ __launch_bounds__(256) void dense_topk_tourney(MergeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char tl_lds[];
   const int row = blockIdx.x;  // = m * K + d; the grid is M * K
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int n = a.nlist * a.kmax;
   float* sv = reinterpret_cast<float*>(tl_lds);
   int* si = reinterpret_cast<int*>(tl_lds + ((n * 4 + 15) & ~15));
   const float* v = a.v + static_cast<int64_t>(row) * n;
   const int32_t* ix = a.ix + static_cast<int64_t>(row) * n;
-  // 16 loads per lane in flight at once: the lists were just written by
-  // workgroups on other XCDs, so every read is a trip to memory
+  // All four waves stage the lists, 16 loads per lane in flight at once (the
+  // lists were just written by workgroups on other XCDs, so every read is a
+  // trip to memory): one round trip up to 4096 entries; then one wave
+  // takes the tournament
   constexpr int U = 16;
-  for (int e0 = 0; e0 < n; e0 += 64 * U) {
+  for (int e0 = 0; e0 < n; e0 += 256 * U) {
     float xv[U];
     int xi[U];
 #pragma unroll
     for (int q = 0; q < U; ++q) {
-      const int e = e0 + lane + 64 * q;
+      const int e = e0 + static_cast<int>(threadIdx.x) + 256 * q;
       xv[q] = e < n ? v[e] : 0.f;
       xi[q] = e < n ? ix[e] : 0;
     }
 #pragma unroll
     for (int q = 0; q < U; ++q) {
-      const int e = e0 + lane + 64 * q;
+      const int e = e0 + static_cast<int>(threadIdx.x) + 256 * q;
       if (e < n) {
         sv[e] = xv[q];
         si[e] = xi[q];
@@ -937,6 +939,7 @@ __global__ __launch_bounds__(64) void dense_topk_tourney(MergeArgs a) {
     }
   }
   __syncthreads();
+  if (threadIdx.x >= 64) return;  // one wave takes the tournament
   float hv[TOURNEY_LPL];
   int hi[TOURNEY_LPL], cur[TOURNEY_LPL];
 #pragma unroll
@@ -1109,7 +1112,7 @@ template <bool LISTS>
 int launch_merge(const MergeArgs& a, int KM, hipStream_t s) {
   if (LISTS && a.nlist <= 64 * TOURNEY_LPL && tourney_lds(a) <= 64 * 1024) {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.M) * a.K));
-    hipLaunchKernelGGL(dense_topk_tourney, grid, dim3(64), tourney_lds(a), s, a);
+    hipLaunchKernelGGL(dense_topk_tourney, grid, dim3(256), tourney_lds(a), s, a);
     return check_launch("dense heads top-k merge");
   }
   const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(a.M) * a.K + 3) / 4));
