@@ -1225,16 +1225,27 @@ extern "C" int medusa_heads_dense(const void* hidden, const void* w1, int64_t w1
   constexpr int RBN = 64;
   a.ntiles = p.big ? (H + B2N - 1) / B2N : (H + RBN - 1) / RBN;
   a.tasks = p.mtiles * a.ntiles * K;
+  // 256 x 256 tiles only while they make at least 128 workgroups: at
+  // vicuna13b-shaped (M = 256, 100 of them) 128 x 64 tiles are faster (dense
+  // heads 714 -> 688 us), at zephyr7b-shaped (M = 512, 160) slower (759 -> 781)
+  const bool big_resid = p.big && a.tasks >= 128;
+  if (p.big && !big_resid) {
+    a.mtiles = (M + 127) / 128;
+    a.ntiles = (H + RBN - 1) / RBN;
+    a.tasks = a.mtiles * a.ntiles * K;
+  }
   a.per_xcd = (a.tasks + 7) / 8;
   a.hid = static_cast<const uint16_t*>(hidden);
   a.r_out = reinterpret_cast<uint16_t*>(w);
-  if (p.big) rc = launch_big<EPI_RESID, 4>(a, stream, "dense heads residual block (256 x 256 tiles)");
+  if (big_resid) rc = launch_big<EPI_RESID, 4>(a, stream, "dense heads residual block (256 x 256 tiles)");
+  else if (p.big) rc = launch_gemm<128, EPI_RESID, 4, RBN>(a, stream, "dense heads residual block");
   else if (p.BM == 64 && (H / BK) % 4 == 0)  // two k-groups: each an even number of k-steps
     rc = launch_gemm<64, EPI_RESID, 4, RBN, 2>(a, stream, "dense heads residual block");
   else if (p.BM == 64) rc = launch_gemm<64, EPI_RESID, 4, RBN>(a, stream, "dense heads residual block");
   else rc = launch_gemm<128, EPI_RESID, 4, RBN>(a, stream, "dense heads residual block");
   if (rc) return rc;
   // stage 2: logits tiles of every head and their per-tile top-kmax
+  a.mtiles = p.mtiles;
   DenseArgs b = a;
   b.x = reinterpret_cast<const uint16_t*>(w);
   b.x_hstride = static_cast<int64_t>(M) * H;
