@@ -1021,10 +1021,10 @@ __global__ __launch_bounds__(512) void tree_attn_gqa(AttnArgs a) {
   // the vector unit.  Softmax does not depend on the reference, so the
   // result is the same wherever the probabilities stay in range.  They do
   // unless a later key's score exceeds the first block's maximum by a wide
-  // margin: the pass is kept if every row's running sum is at most 2^64 and
-  // every output accumulator is finite (then no probability, sum or product
-  // overflowed, and the merge's weights exp2(m - M) l keep their range), and
-  // if every row saw a key in the first block (else its reference is a
+  // margin: the pass is kept if every live row's running sum is at most 2^64
+  // and its output accumulators are finite (then no probability, sum or
+  // product overflowed, and the merge's weights exp2(m - M) l keep their
+  // range), and if it saw a key in the first block (else its reference is a
   // placeholder that later probabilities could underflow against).  If any
   // wave fails, the workgroup computes the split again checking every half,
   // the reference then following the running maximum within RESCALE_SLACK.
