@@ -106,6 +106,33 @@ def test_layers_equal_per_layer_calls(splits, hq, hkv, monkeypatch):
         assert torch.equal(out[l], one), l
 
 
+def test_layers_gqa_recomputed_pass_equal_per_layer(monkeypatch):
+    """The one-workgroup-per-K/V-head kernel in one grid over layers when some
+    workgroups recompute their split: layer 0's keys grow along the sequence
+    (its first pass overflows, so its workgroups compute again checking every
+    half), layer 1's are plain.  At a fixed split count each layer equals its
+    single-layer call bit for bit, and layer 0 matches the oracle."""
+    w = synth.WORKLOADS["zephyr7b-shaped"].scaled(B=2, ctx=1500, cfg_id=321)
+    parent, rank = synth.cost_ordered_tree(w.topk, w.T)
+    t = api.Tree(parent, rank, w.topk)
+    L = 2
+    q, k, v, ctx = _stacked_inputs(w, L, ctx_lens=[1500, 1301])
+    ramp = 1 + 47 * torch.arange(k.shape[3], device=DEV, dtype=torch.float32) / k.shape[3]
+    k[0] = (k[0].float() * ramp[None, None, :, None]).to(torch.bfloat16)
+    monkeypatch.setenv("MEDUSA_ATTN_SPLITS", "2")
+    announce("attention layers, recomputed first pass")
+    out = api.tree_attention_layers(q, k, v, ctx, w.ctx, t)
+    for l in range(L):
+        one = api.tree_attention(q[l], k[l], v[l], ctx, w.ctx, t)
+        torch.cuda.synchronize()
+        assert torch.equal(out[l], one), l
+    vis = otree.visible_bruteforce(parent)
+    ref = oattn.tree_attention(to64(q[0]), to64(k[0]), to64(v[0]), ctx.tolist(), vis)
+    got = to64(out[0])
+    assert np.all(np.isfinite(got))
+    assert row_rel_err(got, ref) <= TOL_BF16
+
+
 @pytest.mark.parametrize("name", ["vicuna7b-shaped", "vicuna13b-shaped", "zephyr7b-shaped"])
 def test_layers_full_size_sampled_rows(name):
     """Every layer of the workload in one call, in the planner's own split
