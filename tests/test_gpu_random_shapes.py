@@ -6,12 +6,17 @@ hand-picked cases of the per-call tests:
   {1, 2, 3, 5, 8}, cache slack, ctx_max above or below the largest context,
   bf16 and fp32; cache slots past each sequence are NaN, so any read beyond
   the sequence shows;
+- tree attention score ranges: random bf16 shapes whose keys are scaled so
+  that later scores rise far above, fall far below or spike above those of
+  a split's first block, at forced split counts;
 - candidates: random vocabulary sizes (from the largest k up to 70000),
   1..6 heads keeping 1..32 candidates, some logits drawn from a handful of
   values so that ties are everywhere;
 - heads: random M (1..70), H, V, K, shared or per-head vocab projection,
   bf16 and fp32.
 Every configuration is printed before it runs."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -64,6 +69,56 @@ def test_attention_random_shapes(seed):
     got = to64(out)
     assert np.all(np.isfinite(got))
     assert row_rel_err(got.reshape(-1, D), ref.reshape(-1, D)) <= (TOL_BF16 if bf16 else TOL_F32)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_attention_random_score_ranges(seed):
+    """Random bf16 shapes (grouped-query ones with more than 128 query rows
+    per K/V head among them) whose keys are scaled along the sequence: rising
+    (later scores far above the first block's: the one-workgroup-per-head
+    kernel keeps its first pass or computes the split again), falling (the
+    reference stays high, later probabilities are small) or a few spiked
+    keys anywhere; forced split counts put the jumps inside and across
+    splits."""
+    rng = np.random.default_rng(9500 + seed)
+    topk, T, parent, rank = _random_tree(rng, max_T=100)
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 4, 8]))
+    ctx = [int(x) for x in rng.integers(0, 1500, size=B)]
+    S_cap = max(ctx) + T + int(rng.integers(0, 20))
+    w = synth.WORKLOADS["vicuna7b-shaped"].scaled(
+        B=B, Hq=G * Hkv, Hkv=Hkv, T=T, K=len(topk), topk=topk, ctx=max(ctx), cfg_id=700 + seed)
+    kind = ("rise", "fall", "spike")[seed % 3]
+    f = float(rng.uniform(2, 60))
+    splits = int(rng.choice([0, 1, 2, 5]))
+    announce("attention random score ranges", seed, dict(B=B, Hkv=Hkv, G=G, T=T, ctx=ctx, kind=kind,
+                                                          f=round(f, 1), splits=splits))
+    tree = api.Tree(parent, rank, topk)
+    q, k, v, ctx_t = synth.attention_inputs(w, 0, DEV, S_cap=S_cap, ctx_lens=ctx)
+    pos = torch.arange(S_cap, device=DEV, dtype=torch.float32) / S_cap
+    if kind == "rise":
+        scale = 1 + (f - 1) * pos
+    elif kind == "fall":
+        scale = f - (f - 1) * pos
+    else:
+        scale = torch.ones(S_cap, device=DEV)
+        scale[torch.from_numpy(rng.integers(0, S_cap, size=3)).to(DEV)] = f
+    k = (k.float() * scale[None, None, :, None]).to(torch.bfloat16).contiguous()
+    for b, c in enumerate(ctx):
+        k[b, :, c + T:] = float("nan")
+        v[b, :, c + T:] = float("nan")
+    if splits:
+        os.environ["MEDUSA_ATTN_SPLITS"] = str(splits)
+    try:
+        out = api.tree_attention(q, k, v, ctx_t, max(ctx), tree)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("MEDUSA_ATTN_SPLITS", None)
+    ref = oattn.tree_attention(to64(q), to64(k), to64(v), ctx, otree.visible_bruteforce(parent))
+    got = to64(out)
+    assert np.all(np.isfinite(got))
+    assert row_rel_err(got.reshape(-1, 128), ref.reshape(-1, 128)) <= TOL_BF16
 
 
 @pytest.mark.parametrize("seed", range(16))
