@@ -561,17 +561,6 @@ __global__ __launch_bounds__(768) void tree_attn_bf16(AttnArgs a) {
   }
 }
 
-// Row group of a merge workgroup.  The attention kernels give XCD x (the
-// workgroups with id % 8 == x) a contiguous eighth of their tasks, which are
-// ordered by (layer, sequence, K/V head); the merge groups are ordered the
-// same way and split into eighths alike, so most partials are read on the
-// XCD whose L2 took them (zephyr7b-shaped: a layer's call ~2 us shorter).
-// Any placement gives the same result.
-__device__ __forceinline__ int64_t merge_group(int64_t nwg) {
-  const int64_t per = (nwg + 7) / 8;
-  return (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-}
-
 // Merge the NS split partials of every query row, in split order (NS <= 64):
 // out = sum_s w_s l_s O_s / sum_s w_s l_s with w_s = exp2(m_s - max_s m_s) and
 // O_s the split's normalised output.  Two rows per wave, 32 lanes per row,
@@ -580,10 +569,7 @@ __device__ __forceinline__ int64_t merge_group(int64_t nwg) {
 __global__ __launch_bounds__(64) void merge_splits(AttnArgs a) {
   const int lane = threadIdx.x & 31;  // lane within the row's half-wave
   const int BH = a.B * a.Hkv;
-  const int64_t nwg = (static_cast<int64_t>(a.L) * BH * a.QR + 1) / 2;
-  const int64_t g = merge_group(nwg);
-  if (g >= nwg) return;  // whole wave
-  const int64_t gr = g * 2 + (threadIdx.x >> 5);
+  const int64_t gr = static_cast<int64_t>(blockIdx.x) * 2 + (threadIdx.x >> 5);
   const bool live = gr < static_cast<int64_t>(a.L) * BH * a.QR;  // both halves reach the shuffles
   const int64_t grc = live ? gr : 0;
   const int lbh = static_cast<int>(grc / a.QR);  // = layer * B * Hkv + bh
@@ -637,10 +623,7 @@ __global__ __launch_bounds__(64) void merge_splits(AttnArgs a) {
 __global__ __launch_bounds__(64) void merge_splits16(AttnArgs a) {
   const int lane = threadIdx.x & 15;  // lane within the row's 16
   const int BH = a.B * a.Hkv;
-  const int64_t nwg = (static_cast<int64_t>(a.L) * BH * a.QR + 3) / 4;
-  const int64_t g = merge_group(nwg);
-  if (g >= nwg) return;  // whole wave
-  const int64_t gr = g * 4 + (threadIdx.x >> 4);
+  const int64_t gr = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 4);
   const bool live = gr < static_cast<int64_t>(a.L) * BH * a.QR;  // every row group reaches the shuffles
   const int64_t grc = live ? gr : 0;
   const int lbh = static_cast<int>(grc / a.QR);
@@ -1380,7 +1363,7 @@ int attention_launch(const void* q, const void* k_cache, const void* v_cache, in
   // workgroup, 32 per merged row)
   const int64_t tasks = static_cast<int64_t>(L) * B * Hkv * p.QC * p.NS;
   const int64_t merge_rows = static_cast<int64_t>(L) * B * Hkv * p.QR;
-  if ((tasks + 7) / 8 * 8 * 768 >= (1ll << 32) || (p.NS > 1 && (merge_rows + 64) * 32 >= (1ll << 32))) {
+  if ((tasks + 7) / 8 * 8 * 768 >= (1ll << 32) || (p.NS > 1 && merge_rows * 32 >= (1ll << 32))) {
     set_error("tree attention grid too large (L*B*Hkv=%lld, %d splits)",
               static_cast<long long>(L) * B * Hkv, p.NS);
     return MEDUSA_EUNSUPPORTED;
@@ -1414,9 +1397,9 @@ int attention_launch(const void* q, const void* k_cache, const void* v_cache, in
   // layer's call ~4.5 us shorter), below that two rows per wave in 8-byte
   // pieces (more waves for few rows)
   if (rows >= 4096)
-    hipLaunchKernelGGL(merge_splits16, dim3(static_cast<unsigned>(8 * (((rows + 3) / 4 + 7) / 8))), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(merge_splits16, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL(merge_splits, dim3(static_cast<unsigned>(8 * (((rows + 1) / 2 + 7) / 8))), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(merge_splits, dim3(static_cast<unsigned>((rows + 1) / 2)), dim3(64), 0, stream, a);
   return check_launch("tree attention split merge");
 }
 
